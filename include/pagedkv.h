@@ -1,0 +1,197 @@
+/*
+ * pagedkv.h - C ABI of the MI355X (gfx950) paged decode-attention library.
+ *
+ * Sources this interface follows (cited by short key throughout):
+ *   [ITH] iThome ithelp article 10405755 on PagedAttention
+ *         (ithelp.ithome.com.tw/articles/10405755).
+ *   [PU]  Fanyi Pu, "Infra: PagedAttention" (pufanyi.com, ml-revisit/infra).
+ *   [AK]  "Paged attention story" (akira.ipas-ai.com, stand-up-comedy series).
+ *
+ * The library implements the decode-time hot path those pages describe: a KV
+ * cache cut into fixed-size physical blocks, reached through a per-sequence
+ * block table, read in place by the attention kernel; a slot-mapped writer
+ * that puts a new token's K/V into its tail slot; and a whole-block copier for
+ * copy-on-write of a shared, partly filled tail block.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless an argument says HOST.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on that stream and returns; nothing
+ *    synchronises.  Results are visible after the stream is synchronised.
+ *  - The library allocates no memory, keeps no pointer after a call returns
+ *    and has no mutable global state: calls on different streams with
+ *    disjoint outputs may run concurrently.
+ *  - bf16 is IEEE bfloat16 (1 sign, 8 exponent, 7 fraction bits) stored as
+ *    16-bit words; fp32 is IEEE binary32.  Rounding to bf16 is
+ *    round-to-nearest-even.
+ *  - Host-checkable preconditions are verified before any HIP call; a
+ *    violation returns an error status and enqueues nothing.  Values that
+ *    live in device memory (table entries, lengths, slots) are the caller's
+ *    contract: out-of-range values there are undefined behaviour, exactly
+ *    like an out-of-range index into any device array.
+ *
+ * Cache layout (one layer; a multi-layer model holds one pair per layer)
+ * ----------------------------------------------------------------------
+ *   P   = num_blocks      physical blocks in the pool      [PU §按 Block 分配]
+ *   B   = block_size      tokens per block
+ *   Hkv = num_kv_heads,  D = head_dim
+ *
+ *   k_cache : bf16 [P, Hkv, B, D]  element (p,h,o,d) at ((p*Hkv + h)*B + o)*D + d
+ *   v_cache : bf16 [P, Hkv, D, B]  element (p,h,o,d) at ((p*Hkv + h)*D + d)*B + o
+ *
+ * K keeps each token's head vector contiguous; V is stored transposed inside
+ * a block so that a run of consecutive tokens of one feature is contiguous
+ * (the operand order of the P.V contraction over tokens).  A (block, head)
+ * tile of either tensor is one contiguous B*D*2-byte range.
+ *
+ * Slots [PU §KV Cache 为什么会浪费显存 defines a slot as the room for one
+ * token's KV; §按 Block 分配 reads position t through logical block t/B and
+ * in-block offset t%B]:  the token at position t of a sequence whose block
+ * table row is bt lives in slot  s = bt[t / B] * B + t % B,  i.e. physical
+ * block s / B, offset s % B.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,     /* null pointer, negative count, inconsistent sizes     */
+  PKV_ERR_UNSUPPORTED = -2, /* a shape or option the kernels do not implement       */
+  PKV_ERR_WORKSPACE = -3,   /* workspace pointer null or smaller than required      */
+  PKV_ERR_HIP = -4          /* a HIP launch or runtime call reported an error       */
+} pkv_status;
+
+typedef enum { PKV_DTYPE_BF16 = 0, PKV_DTYPE_F32 = 1 } pkv_dtype;
+
+/* Which decode kernel family runs.  AUTO picks the matrix-core kernel when the
+ * shape allows it (head_dim 64 or 128, block_size 8/16/32, group <= 16,
+ * partition a multiple of 32) and the generic vector kernel otherwise. */
+typedef enum {
+  PKV_KERNEL_AUTO = 0,
+  PKV_KERNEL_MFMA = 1,    /* error PKV_ERR_UNSUPPORTED if the shape does not fit */
+  PKV_KERNEL_GENERIC = 2  /* any head_dim <= 256, any block_size >= 1, any group  */
+} pkv_kernel;
+
+/* Problem description for pkv_paged_attention_decode. */
+typedef struct {
+  int32_t num_seqs;           /* S  >= 0                                             */
+  int32_t num_q_heads;        /* Hq >= 1                                             */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0; group G = Hq / Hkv         */
+  int32_t head_dim;           /* D                                                   */
+  int32_t num_blocks;         /* P, blocks in the pool (bounds contract)             */
+  int32_t max_blocks_per_seq; /* row stride (in entries) of block_tables, >= 1       */
+  int32_t max_seq_len;        /* host-known bound on every seq_lens[b]; sizes the
+                                 split-KV grid; <= max_blocks_per_seq * block_size   */
+  int32_t partition_size;     /* tokens per split-KV partition, a multiple of
+                                 block_size (and of 32 for the MFMA kernel);
+                                 0 = library choice                                  */
+  pkv_dtype out_dtype;        /* element type of `out`                               */
+  pkv_kernel kernel;          /* kernel family, normally PKV_KERNEL_AUTO              */
+} pkv_decode_dims;
+
+/* Bytes of scratch that pkv_paged_attention_decode needs for `dims` and
+ * `block_size`.  The caller allocates it (device memory, 256-byte aligned);
+ * its contents need no initialisation and are garbage after the call.
+ * Returns 0 when no split-KV merge can be needed, and (size_t)-1 when the
+ * arguments are invalid. */
+size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size);
+
+/* Single-query paged decode attention with GQA [ITH §PagedAttention 的核心想法:
+ * the attention formula is unchanged, the kernel looks the block table up and
+ * reads K,V where the physical blocks are; PU §按 Block 分配: softmax
+ * normalises over every token the query can see, s_i = q.k_i / sqrt(d) (the
+ * scale is an argument here), and per-segment results merge by
+ * o = (Z1 o1 + Z2 o2) / (Z1 + Z2) after rescaling to a common maximum].
+ *
+ *   q            bf16 [S, Hq, D] contiguous; the query of the one position
+ *                being decoded per sequence.
+ *   k_cache      bf16, layout above.     v_cache  bf16, layout above.
+ *   block_tables int32 [S, max_blocks_per_seq]; row b holds physical block ids
+ *                for logical blocks 0 .. ceil(T_b/B)-1, each in [0, P).  Later
+ *                entries are never read.
+ *   seq_lens     int32 [S]; T_b = number of cached tokens of sequence b,
+ *                including the token being decoded (whose K/V must already be
+ *                in the cache).  0 <= T_b <= dims->max_seq_len.
+ *   block_size   B >= 1.   scale  multiplier of q.k (normally 1/sqrt(D)).
+ *   out          [S, Hq, D] contiguous, dims->out_dtype.  Query head h reads
+ *                KV head h / G (consecutive query heads share a KV head).
+ *                A sequence with T_b == 0 gets an all-zero row.
+ *   workspace    device scratch of at least pkv_decode_workspace_size bytes
+ *                (may be NULL when that size is 0).
+ * Only tokens t < T_b are read; cache slots past them and unused blocks may
+ * hold any bits, NaN included, without affecting `out`.
+ * Returns PKV_OK, or an error status with nothing enqueued. */
+pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache,
+                                      const void* v_cache,
+                                      const int32_t* block_tables,
+                                      const int32_t* seq_lens, int32_t block_size,
+                                      float scale, void* out,
+                                      const pkv_decode_dims* dims, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Slot-mapped cache write [ITH §手動畫一次 block table: the next token goes
+ * into the tail block's next free slot; PU §按 Block 分配: new tokens fill the
+ * tail block first].  For n in [0, num_tokens) with s = slot_mapping[n] >= 0:
+ *   K of token n, head h  -> k_cache block s/B, head h, offset s%B
+ *   V of token n, head h  -> v_cache block s/B, head h, offset s%B
+ * Negative slots are skipped (padding tokens).  A bit copy: no rounding.
+ *   k, v          bf16 [num_tokens, num_kv_heads, head_dim] contiguous.
+ *   slot_mapping  int64 [num_tokens]; each s in [-inf, num_blocks*block_size);
+ *                 non-negative slots must be distinct within one call.
+ * head_dim must be a multiple of 8 (16-byte rows). */
+pkv_status pkv_reshape_and_cache(const void* k, const void* v,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 void* k_cache, void* v_cache, int32_t num_blocks,
+                                 int32_t block_size, void* stream);
+
+/* Whole-block copy for copy-on-write of a shared tail block [PU §共享前缀，
+ * 分叉时 Copy-on-write: before a sequence writes into a block whose reference
+ * count is above one, the block is copied and the writer's table entry is
+ * pointed at the copy].  For every layer l and pair i, in both caches:
+ *   cache_l[dst_i] = cache_l[src_i]     (block_bytes bytes each)
+ *   k_caches, v_caches  HOST arrays of num_layers device pointers
+ *                       (1 <= num_layers <= 64), 16-byte aligned.
+ *   block_pairs         device int32 [num_pairs, 2] = (src, dst) block ids.
+ *                       dst ids must be distinct and no dst may also be a src.
+ *   block_bytes         bytes per block per cache, a multiple of 16
+ *                       (Hkv * B * D * 2 for the layout above).
+ * num_pairs == 0 enqueues nothing and returns PKV_OK. */
+pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches,
+                           int32_t num_layers, const int32_t* block_pairs,
+                           int32_t num_pairs, int64_t block_bytes, void* stream);
+
+/* Merge of per-segment attention results [PU §按 Block 分配: with Z_r the sum
+ * of e^{s_i} over segment r and o_r that segment's own softmax output,
+ * o = sum_r Z_r o_r / sum_r Z_r, evaluated after rescaling every Z_r to the
+ * common maximum so nothing overflows].
+ *   part_out  fp32 [num_rows, num_parts, head_dim]: o_r per row and segment.
+ *   part_lse  fp32 [num_rows, num_parts]: ln Z_r; -inf marks an empty segment
+ *             (its part_out entry is then ignored).
+ *   out       [num_rows, head_dim] in out_dtype; a row whose segments are all
+ *             empty becomes 0.
+ * head_dim <= 256. */
+pkv_status pkv_merge_attention_states(const float* part_out, const float* part_lse,
+                                      int32_t num_rows, int32_t num_parts,
+                                      int32_t head_dim, void* out,
+                                      pkv_dtype out_dtype, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pkv_status_string(int32_t status);
+
+/* Version of this ABI: (major << 16) | minor. */
+int32_t pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */
