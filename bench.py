@@ -1,0 +1,212 @@
+"""Benchmark of the paged decode-attention hot path on one MI355X.
+
+One step = one decode step of one layer of the Llama-3.2-1B-shaped batch:
+``reshape_and_cache`` writes the new token of each of the 64 sequences into
+its slot, then ``paged_attention_decode`` attends over every cached token
+(32 q heads / 8 KV heads, head_dim 64, bf16, B = 16, lengths U[128, 2048],
+physical blocks a seeded permutation).  There is no copy-on-write in this
+workload (``copy_blocks`` has no pairs).
+
+Metric: effective KV read GB/s = (sum_b T_b * Hkv * D * 2 tensors * 2 bytes)
+/ step time.  The cache is rotated over enough independent copies (> 1 GiB in
+total) that it cannot sit in the 256 MB Infinity Cache between steps.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+
+Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
+GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+ROTATE_BYTES = 1 << 30
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def bits_to_bf16(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def make_workload(name: str):
+    import workloads
+
+    if name == "llama_b64":
+        return workloads.llama_decode()
+    if name == "long_splitkv":
+        return workloads.long_context()
+    raise SystemExit(f"unknown workload {name!r}")
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    """The oracle as it stands (fp64 C, OpenMP over (sequence, KV head)) on
+    the host cores, over repetitions of the whole step until ~budget_s."""
+    import oracle
+
+    threads = oracle.max_threads()
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 5000:
+        t0 = time.perf_counter()
+        oracle.dense_decode(w.q, w.k_tok, w.v_tok, w.seq_lens, w.scale, num_threads=threads)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per = t_total / reps
+    return {"value": round(w.kv_bytes() / per / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole {w.name} step ({w.total_tokens} tokens x {w.num_kv_heads} KV heads)"
+                      f" repeated {reps}x, {per * 1e3:.1f} ms each, fp64 gather + dense attention"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama_b64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--waves", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: >1 GiB)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(every kernel works on one GPU's share; see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_373_amd as pkv
+    from paged_kv_cache_373_amd.block_manager import slot_mapping_for
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"device {torch.cuda.get_device_name(0)}; generating {args.workload}")
+    w = make_workload(args.workload)
+    s, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    cu = w.cu_seqlens
+    kv_bytes = w.kv_bytes()
+    pool_bytes = 2 * w.num_blocks * hkv * bs * d * 2
+    copies = args.copies or max(2, math.ceil(ROTATE_BYTES / pool_bytes))
+    log(f"{w.total_tokens} tokens, KV bytes/step {kv_bytes / 1e6:.1f} MB, pool "
+        f"{pool_bytes / 1e6:.1f} MB x {copies} copies")
+
+    # Prefill: every cached token except each sequence's last (the one the
+    # step decodes) goes into every copy through the library's writer.
+    seq_ids = np.repeat(np.arange(s), w.seq_lens)
+    pos = np.concatenate([np.arange(t) for t in w.seq_lens])
+    last = cu[1:] - 1
+    slots_all = slot_mapping_for(w.block_tables, seq_ids, pos, bs)
+    prefill = np.ones(len(pos), bool)
+    prefill[last] = False
+    k_all = bits_to_bf16(w.k_tok).to(dev)
+    v_all = bits_to_bf16(w.v_tok).to(dev)
+    slots_prefill = torch.from_numpy(np.where(prefill, slots_all, -1)).to(dev)
+    k_new = k_all[torch.from_numpy(last).to(dev)].contiguous()
+    v_new = v_all[torch.from_numpy(last).to(dev)].contiguous()
+    slots_new = torch.from_numpy(slots_all[last]).to(dev)
+    caches = []
+    for _ in range(copies):
+        kc, vc = pkv.new_kv_cache(w.num_blocks, hkv, bs, d, device=dev, fill=float("nan"))
+        pkv.reshape_and_cache(k_all, v_all, slots_prefill, kc, vc)
+        caches.append((kc, vc))
+    del k_all, v_all
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    q = bits_to_bf16(w.q).to(dev)
+    out = torch.empty((s, hq, d), dtype=torch.bfloat16, device=dev)
+    max_len = int(w.seq_lens.max())
+    ps = args.partition_size or w.partition_size
+    ws_bytes = pkv.decode_workspace_size(q, caches[0][0], bt, max_seq_len=max_len,
+                                         partition_size=ps, waves_per_group=args.waves)
+    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = caches[i % copies]
+        pkv.reshape_and_cache(k_new, v_new, slots_new, kc, vc)
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.paged_attention_decode(q, kc, vc, bt, lens, bs, w.scale, out, max_seq_len=max_len,
+                                   partition_size=ps, waves_per_group=args.waves,
+                                   workspace=workspace)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log(f"step {ms_step * 1e3:.2f} us, decode call {decode_ms * 1e3:.2f} us")
+
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    result = {
+        "metric": "effective KV read GB/s (% of MI355X HBM peak) in paged decode attention",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "num_seqs": s, "num_q_heads": hq, "num_kv_heads": hkv,
+            "head_dim": d, "block_size": bs, "total_tokens": w.total_tokens,
+            "kv_bytes_per_step": kv_bytes, "cache_copies_rotated": copies,
+            "partition_size": ps or "library", "hbm_peak_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+            "tokens_per_s_per_layer_step": round(s / (ms_step * 1e-3), 1),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "paged_attention_decode call (partition kernel + split-KV merge)",
+            "avg_call_us": round(decode_ms * 1e3, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -95,6 +95,8 @@ typedef struct {
                                  0 = library choice                                  */
   pkv_dtype out_dtype;        /* element type of `out`                               */
   pkv_kernel kernel;          /* kernel family, normally PKV_KERNEL_AUTO              */
+  int32_t waves_per_group;    /* matrix-core kernel: wavefronts sharing a partition
+                                 (1, 2 or 4); 0 = library choice; ignored otherwise  */
 } pkv_decode_dims;
 
 /* Bytes of scratch that pkv_paged_attention_decode needs for `dims` and
@@ -126,8 +128,11 @@ size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size
  *                A sequence with T_b == 0 gets an all-zero row.
  *   workspace    device scratch of at least pkv_decode_workspace_size bytes
  *                (may be NULL when that size is 0).
- * Only tokens t < T_b are read; cache slots past them and unused blocks may
- * hold any bits, NaN included, without affecting `out`.
+ * Slots of positions >= T_b in a sequence's last block, and blocks no table
+ * row references, may hold any bits, NaN included: they never reach `out`
+ * (the kernels select them away; they never multiply them by zero).
+ * q, k_cache and v_cache must be 16-byte aligned (PKV_ERR_INVALID otherwise,
+ * for the matrix-core kernel).
  * Returns PKV_OK, or an error status with nothing enqueued. */
 pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache,
                                       const void* v_cache,

@@ -1,0 +1,260 @@
+"""MI355X-native paged decode attention - Python binding of libpagedkv.so.
+
+Thin marshalling over the C ABI in ``include/pagedkv.h``: every function
+checks tensor dtypes/shapes/devices, passes raw device pointers and torch's
+current HIP stream, and raises on a non-zero status.  All arithmetic runs in
+the HIP kernels; nothing here falls back to PyTorch or the CPU.  If the
+library is not built, :func:`lib` raises.
+
+Sources: [ITH] iThome ithelp article 10405755 on PagedAttention; [PU] Fanyi Pu,
+"Infra: PagedAttention" (sections cited per function).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from .block_manager import BlockManager, PoolExhaustedError, slot_mapping_for
+
+__all__ = [
+    "lib", "paged_attention_decode", "reshape_and_cache", "copy_blocks",
+    "merge_attention_states", "decode_workspace_size", "new_kv_cache", "BlockManager",
+    "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4
+_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
+_KERNELS = {"auto": 0, "mfma": 1, "generic": 2}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().pkv_status_string(status).decode()} ({status})")
+
+
+class DecodeDims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("partition_size", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int),
+        ("kernel", ctypes.c_int),
+        ("waves_per_group", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_373_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        dims_p = ctypes.POINTER(DecodeDims)
+        L.pkv_decode_workspace_size.argtypes = [dims_p, i32]
+        L.pkv_decode_workspace_size.restype = sz
+        L.pkv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
+                                                 dims_p, vp, sz, vp]
+        L.pkv_paged_attention_decode.restype = ctypes.c_int
+        L.pkv_reshape_and_cache.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, vp]
+        L.pkv_reshape_and_cache.restype = ctypes.c_int
+        L.pkv_copy_blocks.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i64,
+                                      vp]
+        L.pkv_copy_blocks.restype = ctypes.c_int
+        L.pkv_merge_attention_states.argtypes = [vp, vp, i32, i32, i32, vp, ctypes.c_int, vp]
+        L.pkv_merge_attention_states.restype = ctypes.c_int
+        L.pkv_status_string.argtypes = [i32]
+        L.pkv_status_string.restype = ctypes.c_char_p
+        L.pkv_abi_version.restype = i32
+        _lib = L
+    return _lib
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                 device="cuda", fill: Optional[float] = None):
+    """Allocate (k_cache [P,Hkv,B,D], v_cache [P,Hkv,D,B]) in bf16."""
+    k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=torch.bfloat16,
+                    device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=torch.bfloat16,
+                    device=device)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return k, v
+
+
+def _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
+          waves_per_group) -> DecodeDims:
+    s, hq, d = q.shape
+    p, hkv, bs, _ = k_cache.shape
+    mb = block_tables.shape[1]
+    return DecodeDims(s, hq, hkv, d, p, mb, mb * bs if max_seq_len is None else int(max_seq_len),
+                      int(partition_size), _DTYPES[out_dtype], _KERNELS[kernel],
+                      int(waves_per_group))
+
+
+def decode_workspace_size(q, k_cache, block_tables, *, max_seq_len=None, partition_size=0,
+                          out_dtype=torch.bfloat16, kernel="auto", waves_per_group=0) -> int:
+    dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
+                 waves_per_group)
+    n = lib().pkv_decode_workspace_size(ctypes.byref(dims), k_cache.shape[2])
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID, "pkv_decode_workspace_size")
+    return int(n)
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    key = (device.type, device.index)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                           scale: float, out: torch.Tensor, *, max_seq_len: Optional[int] = None,
+                           partition_size: int = 0, kernel: str = "auto",
+                           waves_per_group: int = 0, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Single-query paged decode attention ([ITH §PagedAttention 的核心想法];
+    [PU §按 Block 分配]).  Writes ``out`` [S, Hq, D] (bf16 or fp32) and returns
+    it.  ``max_seq_len`` defaults to the table capacity (max_blocks * B)."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(v_cache, "v_cache", torch.bfloat16, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(seq_lens, "seq_lens", torch.int32, 1)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, "out", out.dtype, 3)
+    s, hq, d = q.shape
+    p, hkv, bs, d2 = k_cache.shape
+    if bs != block_size or d2 != d or tuple(v_cache.shape) != (p, hkv, d, bs):
+        raise ValueError("cache shapes must be k [P,Hkv,B,D] and v [P,Hkv,D,B] matching q")
+    if tuple(out.shape) != (s, hq, d) or block_tables.shape[0] != s or seq_lens.shape[0] != s:
+        raise ValueError("q, out, block_tables and seq_lens disagree on the batch")
+    dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out.dtype, kernel,
+                 waves_per_group)
+    L = lib()
+    need = L.pkv_decode_workspace_size(ctypes.byref(dims), bs)
+    if need == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID, "pkv_paged_attention_decode")
+    if workspace is None:
+        workspace = _workspace(need, q.device) if need else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = L.pkv_paged_attention_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                      block_tables.data_ptr(), seq_lens.data_ptr(), bs,
+                                      float(scale), out.data_ptr(), ctypes.byref(dims), ws_ptr,
+                                      ws_len, _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_paged_attention_decode")
+    return out
+
+
+def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Write token n's K,V rows into slot slot_mapping[n] (< 0: skipped)
+    ([ITH §手動畫一次 block table]; [PU §按 Block 分配])."""
+    _check(k, "k", torch.bfloat16, 3)
+    _check(v, "v", torch.bfloat16, 3)
+    _check(slot_mapping, "slot_mapping", torch.int64, 1)
+    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(v_cache, "v_cache", torch.bfloat16, 4)
+    n, hkv, d = k.shape
+    p, hkv2, bs, d2 = k_cache.shape
+    if tuple(v.shape) != (n, hkv, d) or slot_mapping.shape[0] != n or (hkv2, d2) != (hkv, d) \
+            or tuple(v_cache.shape) != (p, hkv, d, bs):
+        raise ValueError("reshape_and_cache: inconsistent shapes")
+    st = lib().pkv_reshape_and_cache(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), n, hkv,
+                                     d, k_cache.data_ptr(), v_cache.data_ptr(), p, bs,
+                                     _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_reshape_and_cache")
+
+
+def copy_blocks(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor],
+                block_pairs: torch.Tensor, stream=None) -> None:
+    """cache[dst] = cache[src] in every layer for each (src, dst) row of
+    ``block_pairs`` (int32 [N, 2], on the device) ([PU §共享前缀，分叉时
+    Copy-on-write])."""
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("need one k and one v cache per layer")
+    _check(block_pairs, "block_pairs", torch.int32, 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [N, 2]")
+    shape = tuple(k_caches[0].shape)
+    for kc, vc in zip(k_caches, v_caches):
+        _check(kc, "k_cache", torch.bfloat16, 4)
+        _check(vc, "v_cache", torch.bfloat16, 4)
+        if tuple(kc.shape) != shape or vc.shape[0] != shape[0] or vc.numel() != kc.numel():
+            raise ValueError("all layers must share one cache shape")
+    n_layers = len(k_caches)
+    karr = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in k_caches])
+    varr = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in v_caches])
+    block_bytes = k_caches[0][0].numel() * 2
+    st = lib().pkv_copy_blocks(karr, varr, n_layers, block_pairs.data_ptr(),
+                               block_pairs.shape[0], block_bytes, _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_copy_blocks")
+
+
+def merge_attention_states(part_out: torch.Tensor, part_lse: torch.Tensor,
+                           out: torch.Tensor, stream=None) -> torch.Tensor:
+    """o = sum_r Z_r o_r / sum_r Z_r over segments r, with part_lse = ln Z_r
+    ([PU §按 Block 分配]).  part_out fp32 [R, N, D], part_lse fp32 [R, N],
+    out [R, D] bf16 or fp32."""
+    _check(part_out, "part_out", torch.float32, 3)
+    _check(part_lse, "part_lse", torch.float32, 2)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, "out", out.dtype, 2)
+    r, n, d = part_out.shape
+    if tuple(part_lse.shape) != (r, n) or tuple(out.shape) != (r, d):
+        raise ValueError("merge_attention_states: inconsistent shapes")
+    st = lib().pkv_merge_attention_states(part_out.data_ptr(), part_lse.data_ptr(), r, n, d,
+                                          out.data_ptr(), _DTYPES[out.dtype], _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_merge_attention_states")
+    return out

@@ -1,0 +1,48 @@
+"""Builds libpagedkv.so (HIP kernels + C ABI) for gfx950 with hipcc.
+
+``python -m paged_kv_cache_373_amd.build``.  The library lands next to this
+file, where the Python binding loads it from.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpagedkv.so")
+SOURCES = ["decode.hip", "cache_ops.hip", "api.cpp"]
+ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
+
+# Packed fp32 instructions are kept out of every kernel (-packed-fp32-ops);
+# the host pass warns that it does not know the feature, which is harmless.
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *srcs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if msgs and (verbose or res.returncode != 0):
+        print("\n".join(msgs), file=sys.stderr, flush=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode})")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,224 @@
+// api.cpp - the extern "C" boundary declared in include/pagedkv.h.
+//
+// Every entry point validates what the host can see (pointers, sizes,
+// alignment, workspace) before it touches the HIP runtime; a failed check
+// returns an error status and enqueues nothing.  Then it fills a launch
+// description and calls the launcher of the chosen kernel.
+#include "pagedkv.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <cstddef>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int32_t kAbiMajor = 1;
+constexpr int32_t kAbiMinor = 0;
+constexpr size_t kAlign = 256;
+constexpr int32_t kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Partition length when the caller leaves the choice to the library: long
+// enough that the split-KV merge costs a few percent of the KV traffic, short
+// enough that a batch of moderate sequences yields thousands of workgroups.
+int32_t default_partition(const pkv_decode_dims* d, int32_t block_size) {
+  int32_t ps = d->max_seq_len >= 8192 ? 512 : 256;
+  if (ps % block_size != 0) ps = block_size;  // generic kernel with an odd block size
+  return ps;
+}
+
+struct Plan {
+  bool ok;
+  pkv_status status;
+  int32_t group, partition, num_partitions;
+  bool use_mfma;
+  int waves;
+  size_t part_out_bytes, part_lse_offset, workspace_bytes;
+};
+
+Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
+  Plan p = {};
+  p.status = PKV_ERR_INVALID;
+  if (d == nullptr) return p;
+  if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 ||
+      block_size < 1 || d->num_blocks < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 0 ||
+      d->partition_size < 0)
+    return p;
+  if (d->num_q_heads % d->num_kv_heads != 0) return p;
+  if (static_cast<int64_t>(d->max_seq_len) >
+      static_cast<int64_t>(d->max_blocks_per_seq) * block_size)
+    return p;
+  if (d->out_dtype != PKV_DTYPE_BF16 && d->out_dtype != PKV_DTYPE_F32) return p;
+  if (d->kernel != PKV_KERNEL_AUTO && d->kernel != PKV_KERNEL_MFMA &&
+      d->kernel != PKV_KERNEL_GENERIC)
+    return p;
+  if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
+      d->waves_per_group != 4)
+    return p;
+  if (d->num_seqs > kMaxGridYZ || d->num_kv_heads > kMaxGridYZ || d->num_q_heads > kMaxGridYZ)
+    return (p.status = PKV_ERR_UNSUPPORTED, p);
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.partition = d->partition_size > 0 ? d->partition_size : default_partition(d, block_size);
+  if (p.partition % block_size != 0) return p;
+  const bool mfma_ok =
+      pkv::mfma_shape_supported(d->head_dim, block_size, p.group, p.partition);
+  const bool generic_ok = pkv::generic_shape_supported(d->head_dim, block_size, p.group);
+  if (d->kernel == PKV_KERNEL_MFMA) {
+    if (!mfma_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
+    p.use_mfma = true;
+  } else if (d->kernel == PKV_KERNEL_GENERIC) {
+    if (!generic_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
+    p.use_mfma = false;
+  } else {
+    if (!mfma_ok && !generic_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
+    p.use_mfma = mfma_ok;
+  }
+  // waves per workgroup: each wave should own at least two 32-token chunks
+  if (p.use_mfma) {
+    const int chunks = p.partition / 32;
+    p.waves = d->waves_per_group != 0 ? d->waves_per_group
+                                      : (chunks >= 8 ? 4 : (chunks >= 4 ? 2 : 1));
+  }
+  const int64_t np = (static_cast<int64_t>(d->max_seq_len) + p.partition - 1) / p.partition;
+  p.num_partitions = static_cast<int32_t>(np < 1 ? 1 : np);
+  if (p.num_partitions > 1) {
+    const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * p.num_partitions;
+    p.part_out_bytes = round_up(rows * d->head_dim * sizeof(float), kAlign);
+    p.part_lse_offset = p.part_out_bytes;
+    p.workspace_bytes = p.part_out_bytes + round_up(rows * sizeof(float), kAlign);
+  }
+  p.ok = true;
+  p.status = PKV_OK;
+  return p;
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_abi_version(void) { return (kAbiMajor << 16) | kAbiMinor; }
+
+const char* pkv_status_string(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID: return "PKV_ERR_INVALID: invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: shape or option not implemented";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP: HIP runtime or launch error";
+    default: return "unknown pkv_status";
+  }
+}
+
+size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size) {
+  const Plan p = plan_decode(dims, block_size);
+  if (!p.ok) return static_cast<size_t>(-1);
+  return p.workspace_bytes;
+}
+
+pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int32_t block_size, float scale, void* out,
+                                      const pkv_decode_dims* dims, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  const Plan p = plan_decode(dims, block_size);
+  if (!p.ok) return p.status;
+  if (dims->num_seqs == 0) return PKV_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
+      seq_lens == nullptr || out == nullptr)
+    return PKV_ERR_INVALID;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+  if (p.use_mfma && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)))
+    return PKV_ERR_INVALID;
+  if (p.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < p.workspace_bytes) return PKV_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PKV_ERR_WORKSPACE;
+  }
+  pkv::DecodeLaunch a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.num_seqs = dims->num_seqs;
+  a.prm.num_q_heads = dims->num_q_heads;
+  a.prm.num_kv_heads = dims->num_kv_heads;
+  a.prm.group = p.group;
+  a.prm.head_dim = dims->head_dim;
+  a.prm.block_size = block_size;
+  a.prm.max_blocks_per_seq = dims->max_blocks_per_seq;
+  a.prm.partition_size = p.partition;
+  a.prm.num_partitions = p.num_partitions;
+  a.prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  a.prm.out_f32 = dims->out_dtype == PKV_DTYPE_F32 ? 1 : 0;
+  a.prm.out = out;
+  if (p.workspace_bytes > 0) {
+    char* ws = static_cast<char*>(workspace);
+    a.prm.part_out = reinterpret_cast<float*>(ws);
+    a.prm.part_lse = reinterpret_cast<float*>(ws + p.part_lse_offset);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(p.use_mfma ? pkv::launch_decode_mfma(a, p.waves, s)
+                               : pkv::launch_decode_generic(a, s));
+}
+
+pkv_status pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 void* k_cache, void* v_cache, int32_t num_blocks,
+                                 int32_t block_size, void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 8 || head_dim % 8 != 0 ||
+      num_blocks < 1 || block_size < 1)
+    return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr || k_cache == nullptr ||
+      v_cache == nullptr)
+    return PKV_ERR_INVALID;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PKV_ERR_INVALID;
+  return hip_status(pkv::launch_reshape_and_cache(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slot_mapping, num_tokens,
+      num_kv_heads, head_dim, static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+      block_size, static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                           const int32_t* block_pairs, int32_t num_pairs, int64_t block_bytes,
+                           void* stream) {
+  if (num_pairs < 0 || num_layers < 1 || num_layers > pkv::kMaxCopyLayers || block_bytes <= 0 ||
+      block_bytes % 16 != 0)
+    return PKV_ERR_INVALID;
+  if (num_pairs == 0) return PKV_OK;
+  if (num_pairs > 0x7FFFFFFF / 2 || k_caches == nullptr || v_caches == nullptr ||
+      block_pairs == nullptr)
+    return PKV_ERR_INVALID;
+  for (int32_t l = 0; l < num_layers; ++l)
+    if (k_caches[l] == nullptr || v_caches[l] == nullptr || !aligned16(k_caches[l]) ||
+        !aligned16(v_caches[l]))
+      return PKV_ERR_INVALID;
+  return hip_status(pkv::launch_copy_blocks(k_caches, v_caches, num_layers, block_pairs,
+                                            num_pairs, block_bytes,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_merge_attention_states(const float* part_out, const float* part_lse,
+                                      int32_t num_rows, int32_t num_parts, int32_t head_dim,
+                                      void* out, pkv_dtype out_dtype, void* stream) {
+  if (num_rows < 0 || num_parts < 1 || head_dim < 1 || head_dim > 256) return PKV_ERR_INVALID;
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F32) return PKV_ERR_INVALID;
+  if (num_rows == 0) return PKV_OK;
+  if (part_out == nullptr || part_lse == nullptr || out == nullptr) return PKV_ERR_INVALID;
+  return hip_status(pkv::launch_merge(part_out, part_lse, num_rows, num_parts, num_parts,
+                                      head_dim, nullptr, 1, 1, out,
+                                      out_dtype == PKV_DTYPE_F32 ? 1 : 0,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

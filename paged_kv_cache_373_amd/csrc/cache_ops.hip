@@ -1,0 +1,105 @@
+// cache_ops.hip - the two cache writers of the paged KV cache, for gfx950.
+//
+//   reshape_and_cache  puts token n's K and V rows into slot_mapping[n]
+//                      (iThome ithelp article 10405755 on PagedAttention,
+//                      section "手動畫一次 block table": a new token goes into
+//                      the next free slot of the tail block; Fanyi Pu,
+//                      "Infra: PagedAttention", section "按 Block 分配": the
+//                      slot is physical block t/B's offset t%B).
+//   copy_blocks        copies whole blocks src -> dst in every layer (Fanyi Pu,
+//                      "Infra: PagedAttention", section "共享前缀，分叉时
+//                      Copy-on-write": a shared tail block is duplicated before
+//                      the first diverging write).
+// Both are bit copies: no value is rounded or converted.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// One thread moves 8 features (16 bytes) of one (token, KV head) row.
+// K: one 16-byte store into the token's row of the [B, D] tile.
+// V: the tile is [D, B], so the 8 features go to 8 rows at stride B.
+__global__ void __launch_bounds__(256)
+    reshape_and_cache_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                             const int64_t* __restrict__ slot_mapping, int64_t num_items,
+                             int32_t num_kv_heads, int32_t head_dim, uint16_t* __restrict__ k_cache,
+                             uint16_t* __restrict__ v_cache, int32_t block_size) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (item >= num_items) return;
+  const int32_t chunks = head_dim / 8;
+  const int64_t row = item / chunks;  // (token, head)
+  const int32_t c8 = static_cast<int32_t>(item - row * chunks);
+  const int64_t n = row / num_kv_heads;
+  const int32_t h = static_cast<int32_t>(row - n * num_kv_heads);
+  const int64_t slot = slot_mapping[n];
+  if (slot < 0) return;
+  const int64_t blk = slot / block_size;
+  const int32_t off = static_cast<int32_t>(slot - blk * block_size);
+  const size_t src = static_cast<size_t>(row) * head_dim + 8 * c8;
+  const size_t tile = (static_cast<size_t>(blk) * num_kv_heads + h) * block_size * head_dim;
+
+  const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(k + src);
+  *reinterpret_cast<u32x4_t*>(k_cache + tile + static_cast<size_t>(off) * head_dim + 8 * c8) = kv;
+
+  const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(v + src);
+  uint16_t* vdst = v_cache + tile + static_cast<size_t>(8 * c8) * block_size + off;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vdst[static_cast<size_t>(2 * e) * block_size] = static_cast<uint16_t>(vv[e] & 0xFFFFu);
+    vdst[static_cast<size_t>(2 * e + 1) * block_size] = static_cast<uint16_t>(vv[e] >> 16);
+  }
+}
+
+struct LayerPtrs {
+  u32x4_t* k[kMaxCopyLayers];
+  u32x4_t* v[kMaxCopyLayers];
+};
+
+// grid (pair, layer, K|V); the workgroup streams one block in 16-byte units.
+__global__ void __launch_bounds__(256)
+    copy_blocks_kernel(const LayerPtrs ptrs, const int32_t* __restrict__ block_pairs,
+                       int64_t units_per_block) {
+  const int pair = blockIdx.x;
+  const int layer = blockIdx.y;
+  u32x4_t* base = blockIdx.z == 0 ? ptrs.k[layer] : ptrs.v[layer];
+  const int64_t src = block_pairs[2 * pair];
+  const int64_t dst = block_pairs[2 * pair + 1];
+  const u32x4_t* s = base + src * units_per_block;
+  u32x4_t* d = base + dst * units_per_block;
+  for (int64_t i = threadIdx.x; i < units_per_block; i += blockDim.x) d[i] = s[i];
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache,
+                                    uint16_t* v_cache, int32_t block_size, hipStream_t stream) {
+  const int64_t items = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 8);
+  if (items == 0) return hipSuccess;
+  const int64_t blocks = (items + 255) / 256;
+  reshape_and_cache_kernel<<<dim3(static_cast<uint32_t>(blocks)), 256, 0, stream>>>(
+      k, v, slot_mapping, items, num_kv_heads, head_dim, k_cache, v_cache, block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                              const int32_t* block_pairs, int32_t num_pairs,
+                              int64_t block_bytes, hipStream_t stream) {
+  if (num_pairs == 0) return hipSuccess;
+  LayerPtrs ptrs = {};
+  for (int l = 0; l < num_layers; ++l) {
+    ptrs.k[l] = static_cast<u32x4_t*>(k_caches[l]);
+    ptrs.v[l] = static_cast<u32x4_t*>(v_caches[l]);
+  }
+  const dim3 grid(num_pairs, num_layers, 2);
+  copy_blocks_kernel<<<grid, 256, 0, stream>>>(ptrs, block_pairs, block_bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

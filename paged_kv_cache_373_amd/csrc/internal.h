@@ -1,0 +1,65 @@
+// internal.h - launchers shared by the kernel translation units and the C ABI
+// layer.  Not part of the public interface (see include/pagedkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Everything a decode kernel needs besides the tensor pointers.
+struct DecodeParams {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;              // num_q_heads / num_kv_heads
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t partition_size;     // tokens per split-KV partition
+  int32_t num_partitions;     // grid extent over partitions = ceil(max_seq_len / partition_size)
+  float scale_log2;           // scale * log2(e): scores live in base-2 units inside the kernels
+  int32_t out_f32;            // 1: out is fp32, 0: out is bf16
+  void* out;                  // [S, Hq, D]
+  float* part_out;            // [S, Hq, num_partitions, D]   (only when num_partitions > 1)
+  float* part_lse;            // [S, Hq, num_partitions]
+};
+
+struct DecodeLaunch {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  int32_t num_seqs;
+  DecodeParams prm;
+};
+
+// Shapes the matrix-core kernel is instantiated for.
+bool mfma_shape_supported(int head_dim, int block_size, int group, int partition_size);
+bool generic_shape_supported(int head_dim, int block_size, int group);
+
+// Each launcher enqueues its kernel(s) on `stream` and returns the launch error.
+hipError_t launch_decode_mfma(const DecodeLaunch& a, int waves, hipStream_t stream);
+hipError_t launch_decode_generic(const DecodeLaunch& a, hipStream_t stream);
+
+// Split-KV merge.  With seq_lens != nullptr, row r = b * rows_per_seq + h
+// merges ceil(seq_lens[b] / partition_size) partitions and rows that have at
+// most one partition are skipped (their output was written directly);
+// otherwise every row merges `num_parts` partitions.
+hipError_t launch_merge(const float* part_out, const float* part_lse, int32_t num_rows,
+                        int32_t part_stride, int32_t num_parts, int32_t head_dim,
+                        const int32_t* seq_lens, int32_t rows_per_seq,
+                        int32_t partition_size, void* out, int out_f32, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v,
+                                    const int64_t* slot_mapping, int32_t num_tokens,
+                                    int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache,
+                                    uint16_t* v_cache, int32_t block_size, hipStream_t stream);
+
+constexpr int kMaxCopyLayers = 64;
+hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                              const int32_t* block_pairs, int32_t num_pairs,
+                              int64_t block_bytes, hipStream_t stream);
+
+}  // namespace pkv
