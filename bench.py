@@ -136,9 +136,7 @@ def main() -> int:
     out = torch.empty((s, hq, d), dtype=torch.bfloat16, device=dev)
     max_len = int(w.seq_lens.max())
     ps = args.partition_size or w.partition_size
-    ws_bytes = pkv.decode_workspace_size(q, caches[0][0], bt, max_seq_len=max_len,
-                                         partition_size=ps, waves_per_group=args.waves)
-    workspace = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    workspace = pkv.DecodeWorkspace(device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):

@@ -21,7 +21,7 @@
  *    synchronises.  Results are visible after the stream is synchronised.
  *  - The library allocates no memory, keeps no pointer after a call returns
  *    and has no mutable global state: calls on different streams with
- *    disjoint outputs may run concurrently.
+ *    disjoint outputs and workspaces may run concurrently.
  *  - bf16 is IEEE bfloat16 (1 sign, 8 exponent, 7 fraction bits) stored as
  *    16-bit words; fp32 is IEEE binary32.  Rounding to bf16 is
  *    round-to-nearest-even.
@@ -92,19 +92,39 @@ typedef struct {
                                  split-KV grid; <= max_blocks_per_seq * block_size   */
   int32_t partition_size;     /* tokens per split-KV partition, a multiple of
                                  block_size (and of 32 for the MFMA kernel);
-                                 0 = library choice                                  */
+                                 0 = library choice (balanced, see below)            */
   pkv_dtype out_dtype;        /* element type of `out`                               */
   pkv_kernel kernel;          /* kernel family, normally PKV_KERNEL_AUTO              */
   int32_t waves_per_group;    /* matrix-core kernel: wavefronts sharing a partition
                                  (1, 2 or 4); 0 = library choice; ignored otherwise  */
+  int32_t balance_partitions; /* matrix-core kernel: 0 = every partition but a
+                                 sequence's last holds exactly partition_size
+                                 tokens; 1 = a sequence of T tokens is cut into
+                                 ceil(T / partition_size) partitions that share
+                                 its 32-token chunks evenly.  A library-chosen
+                                 partition_size always balances.                     */
 } pkv_decode_dims;
 
 /* Bytes of scratch that pkv_paged_attention_decode needs for `dims` and
- * `block_size`.  The caller allocates it (device memory, 256-byte aligned);
- * its contents need no initialisation and are garbage after the call.
- * Returns 0 when no split-KV merge can be needed, and (size_t)-1 when the
- * arguments are invalid. */
+ * `block_size`; 0 when no split-KV merge can be needed, (size_t)-1 when the
+ * arguments are invalid.  The caller allocates it (device memory, 256-byte
+ * aligned).  Layout: first a counter region of
+ * pkv_decode_workspace_zeroed_bytes bytes (one 32-bit counter per
+ * (sequence, KV head), padded), then per-partition results.  The counter
+ * region must hold zero bytes when a call starts, and every call leaves it
+ * zero when it completes; the rest of the workspace needs no initialisation
+ * and holds garbage after a call.  So a workspace zero-filled once serves any
+ * number of calls of one shape; before a call whose counter region is larger
+ * than the last call's, zero the bytes up to the new size (the last call may
+ * have left partial results there).  One workspace serves one call at a
+ * time: calls that may overlap (on different streams) need different
+ * workspaces. */
 size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size);
+
+/* Leading bytes of the workspace that must be zero when
+ * pkv_paged_attention_decode starts (and are zero again when it completes);
+ * (size_t)-1 when the arguments are invalid. */
+size_t pkv_decode_workspace_zeroed_bytes(const pkv_decode_dims* dims, int32_t block_size);
 
 /* Single-query paged decode attention with GQA [ITH §PagedAttention 的核心想法:
  * the attention formula is unchanged, the kernel looks the block table up and
@@ -127,7 +147,8 @@ size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size
  *                KV head h / G (consecutive query heads share a KV head).
  *                A sequence with T_b == 0 gets an all-zero row.
  *   workspace    device scratch of at least pkv_decode_workspace_size bytes
- *                (may be NULL when that size is 0).
+ *                whose counter region is zero (see above); may be NULL when
+ *                that size is 0.
  * Slots of positions >= T_b in a sequence's last block, and blocks no table
  * row references, may hold any bits, NaN included: they never reach `out`
  * (the kernels select them away; they never multiply them by zero).

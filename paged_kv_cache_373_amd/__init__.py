@@ -21,7 +21,8 @@ from .block_manager import BlockManager, PoolExhaustedError, slot_mapping_for
 
 __all__ = [
     "lib", "paged_attention_decode", "reshape_and_cache", "copy_blocks",
-    "merge_attention_states", "decode_workspace_size", "new_kv_cache", "BlockManager",
+    "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
+    "BlockManager",
     "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
 ]
 
@@ -51,6 +52,7 @@ class DecodeDims(ctypes.Structure):
         ("out_dtype", ctypes.c_int),
         ("kernel", ctypes.c_int),
         ("waves_per_group", ctypes.c_int32),
+        ("balance_partitions", ctypes.c_int32),
     ]
 
 
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
         dims_p = ctypes.POINTER(DecodeDims)
         L.pkv_decode_workspace_size.argtypes = [dims_p, i32]
         L.pkv_decode_workspace_size.restype = sz
+        L.pkv_decode_workspace_zeroed_bytes.argtypes = [dims_p, i32]
+        L.pkv_decode_workspace_zeroed_bytes.restype = sz
         L.pkv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
         L.pkv_paged_attention_decode.restype = ctypes.c_int
@@ -120,46 +124,97 @@ def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: 
 
 
 def _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
-          waves_per_group) -> DecodeDims:
+          waves_per_group, balance_partitions) -> DecodeDims:
     s, hq, d = q.shape
     p, hkv, bs, _ = k_cache.shape
     mb = block_tables.shape[1]
     return DecodeDims(s, hq, hkv, d, p, mb, mb * bs if max_seq_len is None else int(max_seq_len),
                       int(partition_size), _DTYPES[out_dtype], _KERNELS[kernel],
-                      int(waves_per_group))
+                      int(waves_per_group), int(bool(balance_partitions)))
 
 
 def decode_workspace_size(q, k_cache, block_tables, *, max_seq_len=None, partition_size=0,
-                          out_dtype=torch.bfloat16, kernel="auto", waves_per_group=0) -> int:
+                          out_dtype=torch.bfloat16, kernel="auto", waves_per_group=0,
+                          balance_partitions=False) -> int:
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
-                 waves_per_group)
+                 waves_per_group, balance_partitions)
     n = lib().pkv_decode_workspace_size(ctypes.byref(dims), k_cache.shape[2])
     if n == ctypes.c_size_t(-1).value:
         raise PagedKVError(PKV_ERR_INVALID, "pkv_decode_workspace_size")
     return int(n)
 
 
+def _zero_prefix(buf: torch.Tensor, n: int, stream) -> None:
+    """Clear buf[:n] with a fill kernel on ``stream`` (torch's current stream
+    when None)."""
+    if stream is None:
+        buf[:n].zero_()
+        return
+    st = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
+        _stream(stream))
+    with torch.cuda.stream(st):
+        buf[:n].zero_()
+
+
+class DecodeWorkspace:
+    """Device scratch for :func:`paged_attention_decode` that keeps the C
+    ABI's workspace contract: its leading counter region must be zero when a
+    call starts (each call leaves it zero), and the bytes after it may hold a
+    previous call's partial results.  The object remembers how many leading
+    bytes are known to be zero and clears more (with a fill kernel on the
+    call's stream) only when a call needs a larger counter region.
+
+    ``buffer`` may wrap an existing uint8 device tensor of any contents; by
+    default the workspace allocates and grows its own zero-filled buffer."""
+
+    def __init__(self, buffer: Optional[torch.Tensor] = None, device=None):
+        if buffer is not None:
+            if buffer.dtype != torch.uint8 or not buffer.is_cuda or buffer.dim() != 1:
+                raise ValueError("workspace buffer must be a 1-d uint8 device tensor")
+        self.buffer = buffer
+        self.device = buffer.device if buffer is not None else device
+        self.zeroed = 0  # leading bytes known to be zero
+        self.growable = buffer is None
+
+    def prepare(self, nbytes: int, zeroed_bytes: int, device, stream=None) -> torch.Tensor:
+        if self.buffer is None or self.buffer.numel() < nbytes:
+            if not self.growable:
+                raise ValueError(f"workspace holds {self.buffer.numel()} bytes, call needs {nbytes}")
+            self.buffer = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            self.zeroed = self.buffer.numel()
+        if zeroed_bytes > self.zeroed:
+            _zero_prefix(self.buffer, zeroed_bytes, stream)
+        # after the call: the counter region is zero again, the partial
+        # results behind it are not
+        if nbytes > 0:
+            self.zeroed = zeroed_bytes
+        return self.buffer
+
+
 _ws_cache = {}
 
 
-def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+def _default_workspace(device: torch.device) -> DecodeWorkspace:
     key = (device.type, device.index)
-    buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-        _ws_cache[key] = buf
-    return buf
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = DecodeWorkspace(device=device)
+        _ws_cache[key] = ws
+    return ws
 
 
 def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
                            scale: float, out: torch.Tensor, *, max_seq_len: Optional[int] = None,
                            partition_size: int = 0, kernel: str = "auto",
-                           waves_per_group: int = 0, workspace: Optional[torch.Tensor] = None,
-                           stream=None) -> torch.Tensor:
+                           waves_per_group: int = 0, balance_partitions: bool = False,
+                           workspace=None, stream=None) -> torch.Tensor:
     """Single-query paged decode attention ([ITH §PagedAttention 的核心想法];
     [PU §按 Block 分配]).  Writes ``out`` [S, Hq, D] (bf16 or fp32) and returns
-    it.  ``max_seq_len`` defaults to the table capacity (max_blocks * B)."""
+    it.  ``max_seq_len`` defaults to the table capacity (max_blocks * B).
+    ``workspace`` is a :class:`DecodeWorkspace` (reused across calls; the
+    default is one per device) or a raw uint8 device tensor, whose counter
+    region is then cleared before every call."""
     _check(q, "q", torch.bfloat16, 3)
     _check(k_cache, "k_cache", torch.bfloat16, 4)
     _check(v_cache, "v_cache", torch.bfloat16, 4)
@@ -175,15 +230,27 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     if tuple(out.shape) != (s, hq, d) or block_tables.shape[0] != s or seq_lens.shape[0] != s:
         raise ValueError("q, out, block_tables and seq_lens disagree on the batch")
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out.dtype, kernel,
-                 waves_per_group)
+                 waves_per_group, balance_partitions)
     L = lib()
     need = L.pkv_decode_workspace_size(ctypes.byref(dims), bs)
     if need == ctypes.c_size_t(-1).value:
         raise PagedKVError(PKV_ERR_INVALID, "pkv_paged_attention_decode")
-    if workspace is None:
-        workspace = _workspace(need, q.device) if need else None
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    zeroed = L.pkv_decode_workspace_zeroed_bytes(ctypes.byref(dims), bs)
+    ws_ptr, ws_len = None, 0
+    if need:
+        if workspace is None:
+            workspace = _default_workspace(q.device)
+        if isinstance(workspace, DecodeWorkspace):
+            buf = workspace.prepare(need, zeroed, q.device, stream)
+        else:
+            if workspace.dtype != torch.uint8 or not workspace.is_cuda:
+                raise ValueError("workspace must be a uint8 device tensor or a DecodeWorkspace")
+            buf = workspace
+            if buf.numel() < need:
+                raise ValueError(f"workspace holds {buf.numel()} bytes, call needs {need}")
+            if zeroed:
+                _zero_prefix(buf, zeroed, stream)
+        ws_ptr, ws_len = buf.data_ptr(), buf.numel()
     st = L.pkv_paged_attention_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                       block_tables.data_ptr(), seq_lens.data_ptr(), bs,
                                       float(scale), out.data_ptr(), ctypes.byref(dims), ws_ptr,

@@ -38,9 +38,10 @@ struct Plan {
   bool ok;
   pkv_status status;
   int32_t group, partition, num_partitions;
-  bool use_mfma;
+  bool use_mfma, balanced;
   int waves;
-  size_t part_out_bytes, part_lse_offset, workspace_bytes;
+  // workspace: [counters | partition outputs | (max, sum) pairs]
+  size_t counter_bytes, part_out_offset, part_ml_offset, workspace_bytes;
 };
 
 Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
@@ -62,6 +63,7 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
   if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
       d->waves_per_group != 4)
     return p;
+  if (d->balance_partitions != 0 && d->balance_partitions != 1) return p;
   if (d->num_seqs > kMaxGridYZ || d->num_kv_heads > kMaxGridYZ || d->num_q_heads > kMaxGridYZ)
     return (p.status = PKV_ERR_UNSUPPORTED, p);
   p.group = d->num_q_heads / d->num_kv_heads;
@@ -86,13 +88,18 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
     p.waves = d->waves_per_group != 0 ? d->waves_per_group
                                       : (chunks >= 8 ? 4 : (chunks >= 4 ? 2 : 1));
   }
+  // the matrix-core kernel balances partitions when asked to or when the
+  // library picks the partition length
+  p.balanced = p.use_mfma && (d->balance_partitions == 1 || d->partition_size == 0);
   const int64_t np = (static_cast<int64_t>(d->max_seq_len) + p.partition - 1) / p.partition;
   p.num_partitions = static_cast<int32_t>(np < 1 ? 1 : np);
   if (p.num_partitions > 1) {
     const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * p.num_partitions;
-    p.part_out_bytes = round_up(rows * d->head_dim * sizeof(float), kAlign);
-    p.part_lse_offset = p.part_out_bytes;
-    p.workspace_bytes = p.part_out_bytes + round_up(rows * sizeof(float), kAlign);
+    p.counter_bytes = round_up(static_cast<size_t>(d->num_seqs) * d->num_kv_heads *
+                                   sizeof(uint32_t), kAlign);
+    p.part_out_offset = p.counter_bytes;
+    p.part_ml_offset = p.part_out_offset + round_up(rows * d->head_dim * sizeof(float), kAlign);
+    p.workspace_bytes = p.part_ml_offset + round_up(rows * 2 * sizeof(float), kAlign);
   }
   p.ok = true;
   p.status = PKV_OK;
@@ -122,6 +129,12 @@ size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size
   const Plan p = plan_decode(dims, block_size);
   if (!p.ok) return static_cast<size_t>(-1);
   return p.workspace_bytes;
+}
+
+size_t pkv_decode_workspace_zeroed_bytes(const pkv_decode_dims* dims, int32_t block_size) {
+  const Plan p = plan_decode(dims, block_size);
+  if (!p.ok) return static_cast<size_t>(-1);
+  return p.counter_bytes;
 }
 
 pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -156,14 +169,17 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
   a.prm.block_size = block_size;
   a.prm.max_blocks_per_seq = dims->max_blocks_per_seq;
   a.prm.partition_size = p.partition;
+  a.prm.balanced = p.balanced ? 1 : 0;
   a.prm.num_partitions = p.num_partitions;
   a.prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
   a.prm.out_f32 = dims->out_dtype == PKV_DTYPE_F32 ? 1 : 0;
   a.prm.out = out;
   if (p.workspace_bytes > 0) {
     char* ws = static_cast<char*>(workspace);
-    a.prm.part_out = reinterpret_cast<float*>(ws);
-    a.prm.part_lse = reinterpret_cast<float*>(ws + p.part_lse_offset);
+    a.prm.counters = reinterpret_cast<uint32_t*>(ws);
+    a.prm.part_out = reinterpret_cast<float*>(ws + p.part_out_offset);
+    a.prm.part_lse = reinterpret_cast<float*>(ws + p.part_ml_offset);
+    a.prm.part_ml = reinterpret_cast<float*>(ws + p.part_ml_offset);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(p.use_mfma ? pkv::launch_decode_mfma(a, p.waves, s)

@@ -16,13 +16,19 @@ struct DecodeParams {
   int32_t head_dim;
   int32_t block_size;
   int32_t max_blocks_per_seq;
-  int32_t partition_size;     // tokens per split-KV partition
+  int32_t partition_size;     // tokens per split-KV partition (the longest one when balanced)
+  int32_t balanced;           // 1: a sequence's partitions share its 32-token chunks evenly
   int32_t num_partitions;     // grid extent over partitions = ceil(max_seq_len / partition_size)
   float scale_log2;           // scale * log2(e): scores live in base-2 units inside the kernels
   int32_t out_f32;            // 1: out is fp32, 0: out is bf16
   void* out;                  // [S, Hq, D]
-  float* part_out;            // [S, Hq, num_partitions, D]   (only when num_partitions > 1)
-  float* part_lse;            // [S, Hq, num_partitions]
+  // Split-KV workspace (only when num_partitions > 1).
+  float* part_out;            // [S, Hq, num_partitions, D] partition outputs
+  float* part_lse;            // [S, Hq, num_partitions] ln Z_r (vector kernel)
+  float* part_ml;             // [S, Hq, num_partitions, 2] (max in base-2 units, sum)
+                              // (matrix-core kernel; shares memory with part_lse)
+  uint32_t* counters;         // [S, Hkv] finished partitions per (sequence, KV head);
+                              // zero before and after every call
 };
 
 struct DecodeLaunch {

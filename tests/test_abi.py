@@ -54,7 +54,7 @@ def test_header_compiles_as_c():
 
 
 def test_struct_layout_matches_binding():
-    assert ctypes.sizeof(pkv.DecodeDims) == 11 * 4
+    assert ctypes.sizeof(pkv.DecodeDims) == 12 * 4
 
 
 def test_version_and_status_strings():
@@ -67,7 +67,7 @@ def test_version_and_status_strings():
 def _dims(**kw):
     d = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=64, num_blocks=10,
              max_blocks_per_seq=4, max_seq_len=64, partition_size=0, out_dtype=0, kernel=0,
-             waves_per_group=0)
+             waves_per_group=0, balance_partitions=0)
     d.update(kw)
     return pkv.DecodeDims(**d)
 
@@ -82,8 +82,14 @@ BAD = ctypes.c_size_t(-1).value
 def test_workspace_size_rules():
     assert ws(_dims()) == 0  # 64 tokens fit one 256-token partition
     d = _dims(max_seq_len=64, partition_size=32)
-    # 2 partitions: o [2*32*2*64] fp32 + lse [2*32*2] fp32, each 256-aligned
-    assert ws(d) == 2 * 32 * 2 * 64 * 4 + 512
+    # 2 partitions: counters [2*8] u32, outputs [2*32*2*64] fp32 and (max, sum)
+    # pairs [2*32*2*2] fp32, each region rounded up to 256 bytes
+    assert ws(d) == 256 + 2 * 32 * 2 * 64 * 4 + 2 * 32 * 2 * 2 * 4
+    assert pkv.lib().pkv_decode_workspace_zeroed_bytes(ctypes.byref(d), 16) == 256
+    assert pkv.lib().pkv_decode_workspace_zeroed_bytes(ctypes.byref(_dims()), 16) == 0
+    big = _dims(num_seqs=100, max_seq_len=64, partition_size=32)
+    assert pkv.lib().pkv_decode_workspace_zeroed_bytes(ctypes.byref(big), 16) == 3328  # 3200 -> 256k
+    assert ws(_dims(balance_partitions=2)) == BAD
     assert ws(_dims(num_q_heads=30)) == BAD  # Hq % Hkv != 0
     assert ws(_dims(max_seq_len=65)) == BAD  # longer than the table holds
     assert ws(_dims(partition_size=24)) == BAD  # not a multiple of B

@@ -65,13 +65,15 @@ def test_decode_small(name, kernel):
 
 @pytest.mark.parametrize("ps", [32, 64, 96, 256, 512, 1024])
 @pytest.mark.parametrize("waves", [1, 2, 4])
-def test_decode_partition_and_wave_sweep(ps, waves):
-    say(f"case sweep ps={ps} waves={waves}")
+@pytest.mark.parametrize("balanced", [False, True])
+def test_decode_partition_and_wave_sweep(ps, waves, balanced):
+    say(f"case sweep ps={ps} waves={waves} balanced={balanced}")
     w = workloads.random_small(30, 6, 16, 4, 64, 16, 1100, min_len=1)
     g, o = GpuSide(w), OracleSide(w)
     ref = o.decode()
-    out = g.decode(torch.float32, kernel="mfma", partition_size=ps, waves_per_group=waves)
-    compare(out.cpu().numpy(), ref, strict_abs=True, what=f"ps{ps}/w{waves}")
+    out = g.decode(torch.float32, kernel="mfma", partition_size=ps, waves_per_group=waves,
+                   balance_partitions=balanced)
+    compare(out.cpu().numpy(), ref, strict_abs=True, what=f"ps{ps}/w{waves}/bal{balanced}")
 
 
 def test_decode_generic_partitions():
@@ -186,3 +188,36 @@ def test_negative_slots_are_skipped():
     oracle.write_cache(ko, vo, bf16_bits(k), bf16_bits(k), slots.cpu().numpy())
     np.testing.assert_array_equal(bf16_bits(kc), ko)
     np.testing.assert_array_equal(bf16_bits(vc), vo)
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves split-KV calls of changing shapes back to back:
+    leftover partial results of one shape land where the next shape keeps its
+    counters.  A DecodeWorkspace wrapping a buffer of random bytes clears its
+    counter region only when a call needs more of it; a raw tensor gets its
+    counter region cleared before every call."""
+    say("case workspace reuse across shapes")
+    cases = [workloads.random_small(40, 5, 16, 4, 64, 16, 900, min_len=1),
+             workloads.random_small(41, 9, 8, 2, 64, 16, 1500, min_len=1),
+             workloads.random_small(42, 3, 16, 2, 128, 32, 1200, min_len=1),
+             workloads.random_small(43, 12, 32, 8, 64, 8, 600, min_len=1)]
+    sides = [(GpuSide(w), OracleSide(w)) for w in cases]
+    refs = [o.decode() for _, o in sides]
+    g = torch.Generator().manual_seed(44)
+    raw = torch.randint(0, 256, (8 << 20,), dtype=torch.uint8, generator=g).to(DEV)
+    tracked = pkv.DecodeWorkspace(raw.clone())
+    for rnd in range(3):
+        for i, (gs, _) in enumerate(sides):
+            for label, ws in (("tracked", tracked), ("raw", raw)):
+                for balanced in (False, True):
+                    out = gs.decode(torch.float32, partition_size=64, workspace=ws,
+                                    balance_partitions=balanced)
+                    compare(out.cpu().numpy(), refs[i], strict_abs=True,
+                            what=f"ws {label} round {rnd} case {i} balanced={balanced}")
+    # every counter region a call used is zero again afterwards
+    for i, (gs, _) in enumerate(sides):
+        w = gs.w
+        dims = pkv._dims(gs.q, gs.kc, gs.bt, int(w.seq_lens.max()), 64, torch.float32, "auto", 0,
+                         False)
+        z = pkv.lib().pkv_decode_workspace_zeroed_bytes(pkv.ctypes.byref(dims), w.block_size)
+        assert int(raw[:z].count_nonzero()) == 0
