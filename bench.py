@@ -14,11 +14,18 @@ total) that it cannot sit in the 256 MB Infinity Cache between steps.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
-GPU.
+GPU.  ``roofline.achieved`` is the decode launch alone (HIP events on the
+stream it runs on); ``roofline.traffic`` is the HBM bytes per launch measured
+with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by the same counters
+on a plain copy of known size) as recorded in profiles/pmc_traffic.json, and
+null when the decode source has changed since then.
+
+    python bench.py --calibrate-copy 256   # a plain 256 MiB copy, for counter scaling
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -33,6 +40,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 ROTATE_BYTES = 1 << 30
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_373_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
 def log(msg: str) -> None:
@@ -53,6 +62,41 @@ def make_workload(name: str):
     if name == "long_splitkv":
         return workloads.long_context()
     raise SystemExit(f"unknown workload {name!r}")
+
+
+def source_digest() -> str:
+    with open(DECODE_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per decode launch from the committed counter record, if it
+    was taken on this workload and kernel with the current decode source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("kernel") != kernel:
+        return None
+    if rec.get("decode_source_sha256") != source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy(mib: int, reps: int) -> int:
+    """A plain device-to-device copy of `mib` MiB, `reps` times: the known-size
+    reference for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "reps": reps}), flush=True)
+    return 0
 
 
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
@@ -84,6 +128,9 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: >1 GiB)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "generic"])
+    ap.add_argument("--stream-waves", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -92,6 +139,9 @@ def main() -> int:
               "(every kernel works on one GPU's share; see DESIGN.md for how it would shard).",
               file=sys.stderr)
         return 2
+
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, max(args.steps, 1))
 
     import torch
 
@@ -146,6 +196,7 @@ def main() -> int:
             ev[0].record(stream)
         pkv.paged_attention_decode(q, kc, vc, bt, lens, bs, w.scale, out, max_seq_len=max_len,
                                    partition_size=ps, waves_per_group=args.waves,
+                                   kernel=args.kernel, stream_waves=args.stream_waves,
                                    workspace=workspace)
         if ev is not None:
             ev[1].record(stream)
@@ -172,6 +223,8 @@ def main() -> int:
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
+    kernel_name = {"auto": "stream" if not ps else "mfma"}.get(args.kernel, args.kernel)
+    traffic = measured_traffic(w.name, kernel_name)
     result = {
         "metric": "effective KV read GB/s (% of MI355X HBM peak) in paged decode attention",
         "value": round(value, 2),
@@ -189,14 +242,16 @@ def main() -> int:
             "workload": w.name, "num_seqs": s, "num_q_heads": hq, "num_kv_heads": hkv,
             "head_dim": d, "block_size": bs, "total_tokens": w.total_tokens,
             "kv_bytes_per_step": kv_bytes, "cache_copies_rotated": copies,
-            "partition_size": ps or "library", "hbm_peak_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+            "partition_size": ps or "library", "kernel": kernel_name,
+            "hbm_peak_frac_of_step": round(value / HBM_PEAK_GBS, 4),
             "tokens_per_s_per_layer_step": round(s / (ms_step * 1e-3), 1),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "paged_attention_decode call (partition kernel + split-KV merge)",
-            "avg_call_us": round(decode_ms * 1e3, 3),
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": f"paged_attention_decode ({kernel_name} kernel, one launch)",
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "avg_launch_us": round(decode_ms * 1e3, 3),
         },
     }
     if not args.no_cpu_baseline:

@@ -71,13 +71,23 @@ typedef enum {
 
 typedef enum { PKV_DTYPE_BF16 = 0, PKV_DTYPE_F32 = 1 } pkv_dtype;
 
-/* Which decode kernel family runs.  AUTO picks the matrix-core kernel when the
- * shape allows it (head_dim 64 or 128, block_size 8/16/32, group <= 16,
- * partition a multiple of 32) and the generic vector kernel otherwise. */
+/* Which decode kernel family runs.
+ *   STREAM   matrix-core kernel that deals the call's (sequence, KV head,
+ *            32-token chunk) work out evenly to a fixed set of wavefronts;
+ *            head_dim 64 or 128, block_size 8/16/32, group <= 16,
+ *            num_seqs <= 2048.  Ignores partition_size.
+ *   MFMA     matrix-core kernel over split-KV partitions of partition_size
+ *            tokens (a multiple of 32, at most 128 blocks); same head_dim,
+ *            block_size and group limits.
+ *   GENERIC  vector kernel: any head_dim <= 256, block_size >= 1, group.
+ * AUTO picks STREAM when partition_size is 0 and the shape allows it, then
+ * MFMA, then GENERIC.  An explicit family whose limits the shape exceeds
+ * gives PKV_ERR_UNSUPPORTED. */
 typedef enum {
   PKV_KERNEL_AUTO = 0,
-  PKV_KERNEL_MFMA = 1,    /* error PKV_ERR_UNSUPPORTED if the shape does not fit */
-  PKV_KERNEL_GENERIC = 2  /* any head_dim <= 256, any block_size >= 1, any group  */
+  PKV_KERNEL_MFMA = 1,
+  PKV_KERNEL_GENERIC = 2,
+  PKV_KERNEL_STREAM = 3
 } pkv_kernel;
 
 /* Problem description for pkv_paged_attention_decode. */
@@ -103,6 +113,9 @@ typedef struct {
                                  ceil(T / partition_size) partitions that share
                                  its 32-token chunks evenly.  A library-chosen
                                  partition_size always balances.                     */
+  int32_t stream_waves;       /* stream kernel: wavefronts launched, a multiple of 4
+                                 (each takes an equal share of the work);
+                                 0 = library choice                                  */
 } pkv_decode_dims;
 
 /* Bytes of scratch that pkv_paged_attention_decode needs for `dims` and

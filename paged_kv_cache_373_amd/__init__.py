@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1}
-_KERNELS = {"auto": 0, "mfma": 1, "generic": 2}
+_KERNELS = {"auto": 0, "mfma": 1, "generic": 2, "stream": 3}
 
 
 class PagedKVError(RuntimeError):
@@ -53,6 +53,7 @@ class DecodeDims(ctypes.Structure):
         ("kernel", ctypes.c_int),
         ("waves_per_group", ctypes.c_int32),
         ("balance_partitions", ctypes.c_int32),
+        ("stream_waves", ctypes.c_int32),
     ]
 
 
@@ -124,20 +125,20 @@ def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: 
 
 
 def _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
-          waves_per_group, balance_partitions) -> DecodeDims:
+          waves_per_group, balance_partitions, stream_waves=0) -> DecodeDims:
     s, hq, d = q.shape
     p, hkv, bs, _ = k_cache.shape
     mb = block_tables.shape[1]
     return DecodeDims(s, hq, hkv, d, p, mb, mb * bs if max_seq_len is None else int(max_seq_len),
                       int(partition_size), _DTYPES[out_dtype], _KERNELS[kernel],
-                      int(waves_per_group), int(bool(balance_partitions)))
+                      int(waves_per_group), int(bool(balance_partitions)), int(stream_waves))
 
 
 def decode_workspace_size(q, k_cache, block_tables, *, max_seq_len=None, partition_size=0,
                           out_dtype=torch.bfloat16, kernel="auto", waves_per_group=0,
-                          balance_partitions=False) -> int:
+                          balance_partitions=False, stream_waves=0) -> int:
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
-                 waves_per_group, balance_partitions)
+                 waves_per_group, balance_partitions, stream_waves)
     n = lib().pkv_decode_workspace_size(ctypes.byref(dims), k_cache.shape[2])
     if n == ctypes.c_size_t(-1).value:
         raise PagedKVError(PKV_ERR_INVALID, "pkv_decode_workspace_size")
@@ -208,7 +209,8 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            scale: float, out: torch.Tensor, *, max_seq_len: Optional[int] = None,
                            partition_size: int = 0, kernel: str = "auto",
                            waves_per_group: int = 0, balance_partitions: bool = False,
-                           workspace=None, stream=None) -> torch.Tensor:
+                           stream_waves: int = 0, workspace=None,
+                           stream=None) -> torch.Tensor:
     """Single-query paged decode attention ([ITH §PagedAttention 的核心想法];
     [PU §按 Block 分配]).  Writes ``out`` [S, Hq, D] (bf16 or fp32) and returns
     it.  ``max_seq_len`` defaults to the table capacity (max_blocks * B).
@@ -230,7 +232,7 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     if tuple(out.shape) != (s, hq, d) or block_tables.shape[0] != s or seq_lens.shape[0] != s:
         raise ValueError("q, out, block_tables and seq_lens disagree on the batch")
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out.dtype, kernel,
-                 waves_per_group, balance_partitions)
+                 waves_per_group, balance_partitions, stream_waves)
     L = lib()
     need = L.pkv_decode_workspace_size(ctypes.byref(dims), bs)
     if need == ctypes.c_size_t(-1).value:

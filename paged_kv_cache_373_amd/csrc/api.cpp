@@ -25,21 +25,32 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Partition length when the caller leaves the choice to the library: long
-// enough that the split-KV merge costs a few percent of the KV traffic, short
-// enough that a batch of moderate sequences yields thousands of workgroups.
+// Partition length of the partitioned kernels when the caller leaves the
+// choice to the library (the stream kernel has no partitions): long enough
+// that the split-KV merge costs a few percent of the KV traffic, short enough
+// that a batch of moderate sequences yields thousands of workgroups.
 int32_t default_partition(const pkv_decode_dims* d, int32_t block_size) {
   int32_t ps = d->max_seq_len >= 8192 ? 512 : 256;
   if (ps % block_size != 0) ps = block_size;  // generic kernel with an odd block size
   return ps;
 }
 
+enum Family { kGeneric, kMfma, kStream };
+
+// Wavefronts the stream kernel launches by default: 8 per compute unit of an
+// MI355X (256 CUs), enough bytes in flight to saturate HBM with every
+// wavefront resident from the start; fewer when the problem is small.
+constexpr int32_t kStreamWaveTarget = 2048;
+constexpr int32_t kMinChunksPerWave = 4;
+
 struct Plan {
   bool ok;
   pkv_status status;
   int32_t group, partition, num_partitions;
-  bool use_mfma, balanced;
-  int waves;
+  Family family;
+  bool balanced;
+  int waves;         // partitioned kernel: waves per workgroup
+  int stream_waves;  // stream kernel: wavefronts launched
   // workspace: [counters | partition outputs | (max, sum) pairs]
   size_t counter_bytes, part_out_offset, part_ml_offset, workspace_bytes;
 };
@@ -58,48 +69,87 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
     return p;
   if (d->out_dtype != PKV_DTYPE_BF16 && d->out_dtype != PKV_DTYPE_F32) return p;
   if (d->kernel != PKV_KERNEL_AUTO && d->kernel != PKV_KERNEL_MFMA &&
-      d->kernel != PKV_KERNEL_GENERIC)
+      d->kernel != PKV_KERNEL_GENERIC && d->kernel != PKV_KERNEL_STREAM)
     return p;
   if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
       d->waves_per_group != 4)
     return p;
   if (d->balance_partitions != 0 && d->balance_partitions != 1) return p;
+  if (d->stream_waves < 0 || d->stream_waves % 4 != 0) return p;
   if (d->num_seqs > kMaxGridYZ || d->num_kv_heads > kMaxGridYZ || d->num_q_heads > kMaxGridYZ)
     return (p.status = PKV_ERR_UNSUPPORTED, p);
   p.group = d->num_q_heads / d->num_kv_heads;
   p.partition = d->partition_size > 0 ? d->partition_size : default_partition(d, block_size);
   if (p.partition % block_size != 0) return p;
+  const bool stream_ok =
+      pkv::stream_shape_supported(d->head_dim, block_size, p.group, d->num_seqs);
   const bool mfma_ok =
       pkv::mfma_shape_supported(d->head_dim, block_size, p.group, p.partition);
   const bool generic_ok = pkv::generic_shape_supported(d->head_dim, block_size, p.group);
-  if (d->kernel == PKV_KERNEL_MFMA) {
-    if (!mfma_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
-    p.use_mfma = true;
-  } else if (d->kernel == PKV_KERNEL_GENERIC) {
-    if (!generic_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
-    p.use_mfma = false;
-  } else {
-    if (!mfma_ok && !generic_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
-    p.use_mfma = mfma_ok;
+  switch (d->kernel) {
+    case PKV_KERNEL_STREAM:
+      if (!stream_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
+      p.family = kStream;
+      break;
+    case PKV_KERNEL_MFMA:
+      if (!mfma_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
+      p.family = kMfma;
+      break;
+    case PKV_KERNEL_GENERIC:
+      if (!generic_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
+      p.family = kGeneric;
+      break;
+    default:
+      if (d->partition_size == 0 && stream_ok)
+        p.family = kStream;
+      else if (mfma_ok)
+        p.family = kMfma;
+      else if (generic_ok)
+        p.family = kGeneric;
+      else
+        return (p.status = PKV_ERR_UNSUPPORTED, p);
   }
-  // waves per workgroup: each wave should own at least two 32-token chunks
-  if (p.use_mfma) {
-    const int chunks = p.partition / 32;
-    p.waves = d->waves_per_group != 0 ? d->waves_per_group
-                                      : (chunks >= 8 ? 4 : (chunks >= 4 ? 2 : 1));
-  }
-  // the matrix-core kernel balances partitions when asked to or when the
-  // library picks the partition length
-  p.balanced = p.use_mfma && (d->balance_partitions == 1 || d->partition_size == 0);
-  const int64_t np = (static_cast<int64_t>(d->max_seq_len) + p.partition - 1) / p.partition;
-  p.num_partitions = static_cast<int32_t>(np < 1 ? 1 : np);
-  if (p.num_partitions > 1) {
-    const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * p.num_partitions;
-    p.counter_bytes = round_up(static_cast<size_t>(d->num_seqs) * d->num_kv_heads *
-                                   sizeof(uint32_t), kAlign);
+  const size_t units = static_cast<size_t>(d->num_seqs) * d->num_kv_heads;
+  const size_t counter_bytes = round_up(units * sizeof(uint32_t), kAlign);
+  if (p.family == kStream) {
+    // chunks the call can hold at most, and the wavefronts to share them
+    const int64_t chunk_bound =
+        static_cast<int64_t>(units) * ((static_cast<int64_t>(d->max_seq_len) + 31) / 32);
+    int64_t wv = d->stream_waves;
+    if (wv == 0) {
+      wv = (chunk_bound + kMinChunksPerWave - 1) / kMinChunksPerWave;
+      wv = wv < kStreamWaveTarget ? wv : kStreamWaveTarget;
+      wv = (wv + 3) / 4 * 4;
+      if (wv < 4) wv = 4;
+    }
+    p.stream_waves = static_cast<int>(wv);
+    p.num_partitions = 1;
+    // [counters | per-piece (acc) slots | per-piece (max, sum) slots]
+    const size_t slots = units + static_cast<size_t>(p.stream_waves);
+    p.counter_bytes = counter_bytes;
     p.part_out_offset = p.counter_bytes;
-    p.part_ml_offset = p.part_out_offset + round_up(rows * d->head_dim * sizeof(float), kAlign);
-    p.workspace_bytes = p.part_ml_offset + round_up(rows * 2 * sizeof(float), kAlign);
+    p.part_ml_offset = p.part_out_offset +
+                       round_up(slots * p.group * d->head_dim * sizeof(float), kAlign);
+    p.workspace_bytes = p.part_ml_offset + round_up(slots * p.group * 2 * sizeof(float), kAlign);
+  } else {
+    // waves per workgroup: each wave should own at least two 32-token chunks
+    if (p.family == kMfma) {
+      const int chunks = p.partition / 32;
+      p.waves = d->waves_per_group != 0 ? d->waves_per_group
+                                        : (chunks >= 8 ? 4 : (chunks >= 4 ? 2 : 1));
+    }
+    // the matrix-core kernel balances partitions when asked to
+    p.balanced = p.family == kMfma && d->balance_partitions == 1;
+    const int64_t np = (static_cast<int64_t>(d->max_seq_len) + p.partition - 1) / p.partition;
+    p.num_partitions = static_cast<int32_t>(np < 1 ? 1 : np);
+    if (p.num_partitions > 1) {
+      // [counters | partition outputs | (max, sum) pairs]
+      const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * p.num_partitions;
+      p.counter_bytes = counter_bytes;
+      p.part_out_offset = p.counter_bytes;
+      p.part_ml_offset = p.part_out_offset + round_up(rows * d->head_dim * sizeof(float), kAlign);
+      p.workspace_bytes = p.part_ml_offset + round_up(rows * 2 * sizeof(float), kAlign);
+    }
   }
   p.ok = true;
   p.status = PKV_OK;
@@ -149,7 +199,7 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
       seq_lens == nullptr || out == nullptr)
     return PKV_ERR_INVALID;
   if (!std::isfinite(scale)) return PKV_ERR_INVALID;
-  if (p.use_mfma && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)))
+  if (p.family != kGeneric && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)))
     return PKV_ERR_INVALID;
   if (p.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < p.workspace_bytes) return PKV_ERR_WORKSPACE;
@@ -162,6 +212,7 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.num_seqs = dims->num_seqs;
+  a.prm.num_seqs = dims->num_seqs;
   a.prm.num_q_heads = dims->num_q_heads;
   a.prm.num_kv_heads = dims->num_kv_heads;
   a.prm.group = p.group;
@@ -182,8 +233,11 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
     a.prm.part_ml = reinterpret_cast<float*>(ws + p.part_ml_offset);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(p.use_mfma ? pkv::launch_decode_mfma(a, p.waves, s)
-                               : pkv::launch_decode_generic(a, s));
+  switch (p.family) {
+    case kStream: return hip_status(pkv::launch_decode_stream(a, p.stream_waves, s));
+    case kMfma: return hip_status(pkv::launch_decode_mfma(a, p.waves, s));
+    default: return hip_status(pkv::launch_decode_generic(a, s));
+  }
 }
 
 pkv_status pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,

@@ -13,14 +13,20 @@
 //         should synchronise little.
 //
 // Kernel families
-//   decode_mfma     one workgroup per (partition, KV head, sequence); its NW
-//                   wavefronts stride over 32-token chunks of the partition.
-//                   QK^T and P.V run on v_mfma_f32_16x16x32_bf16; the online
-//                   softmax runs on the vector ALU; waves merge through LDS.
+//   decode_stream   matrix-core kernel, the default.  The work of a call -
+//                   every (sequence, KV head) unit cut into 32-token chunks -
+//                   is dealt out in equal contiguous shares to a fixed set of
+//                   wavefronts, so all of them stream HBM until the end; a unit
+//                   cut between wavefronts is merged by the last of them.
+//   decode_mfma     matrix-core kernel over fixed partitions: one workgroup
+//                   per (partition, KV head, sequence), its waves taking the
+//                   partition's chunks round robin, split sequences merged by
+//                   the last partition to finish.
 //   decode_generic  one wavefront per (partition, q head, sequence), scalar
 //                   fp32 online softmax; any head_dim <= 256, any block size.
 //   merge_states    one wavefront per (sequence, q head): combines partition
-//                   results (o_r, ln Z_r) into the output.
+//                   results (o_r, ln Z_r) into the output (vector kernel path
+//                   and the standalone merge entry point).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -45,7 +51,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // exchange) therefore happens a handful of times per partition, not per chunk.
 constexpr float kRescaleThreshold = 8.0f;
 
-// 32-token chunks each wavefront of the matrix-core kernel keeps in flight.
+// 32-token chunks each wavefront of the matrix-core kernels keeps in flight.
 #ifndef PKV_PIPELINE_DEPTH
 #define PKV_PIPELINE_DEPTH 2
 #endif
@@ -77,6 +83,28 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Reads of partials through a buffer resource with the device-coherence cache
+// policy (the same bit an agent-scope atomic load carries).  Unlike atomic
+// loads the compiler keeps many of these in flight at once, which is what a
+// merge over many partials needs.  Offsets are in bytes and stay below
+// `bytes`; the resource's fourth word is the raw 32-bit data format of gfx9.
+struct CoherentReader {
+  static constexpr int kRsrcWord3 = 0x00020000;
+  static constexpr int kDeviceCoherent = 16;  // SC1
+  __amdgpu_buffer_rsrc_t rsrc;
+  __device__ CoherentReader(const void* base, uint32_t bytes)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                               kRsrcWord3)) {}
+  __device__ float f32(uint32_t off) const {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, kDeviceCoherent));
+  }
+  __device__ f32x4_t f32x4(uint32_t off) const {
+    return __builtin_bit_cast(f32x4_t,
+                              __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kDeviceCoherent));
+  }
+};
+
 __device__ __forceinline__ void store_out(void* out, size_t idx, float v, int out_f32) {
   if (out_f32)
     static_cast<float*>(out)[idx] = v;
@@ -84,9 +112,9 @@ __device__ __forceinline__ void store_out(void* out, size_t idx, float v, int ou
     static_cast<uint16_t*>(out)[idx] = float_to_bf16_bits(v);
 }
 
-// Finishes one (sequence, q head) row of a partition: either the final output
-// (single partition) or the partition's (o_r, ln Z_r).  `m2` is the maximum in
-// base-2 units, `den` the sum of 2^(x - m2).
+// Finishes one (sequence, q head) row of a vector-kernel partition: either the
+// final output (single partition) or the partition's (o_r, ln Z_r).  `m2` is
+// the maximum in base-2 units, `den` the sum of 2^(x - m2).
 __device__ __forceinline__ void write_partition_result(const DecodeParams& prm, int b, int hq,
                                                        int p, int nparts, int d, float o,
                                                        float m2, float den, bool empty) {
@@ -102,14 +130,13 @@ __device__ __forceinline__ void write_partition_result(const DecodeParams& prm, 
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel.
+// The matrix-core chunk step shared by decode_stream and decode_mfma.
 //
-// One workgroup per (partition, KV head, sequence); its NW wavefronts take the
-// partition's 32-token chunks round robin (wave w: chunks w, w + NW, ...).
-//
-// Lane roles inside a wavefront (lane = 16 c + r, c in 0..3, r in 0..15):
+// A wavefront consumes a KV head's tokens 32 at a time (a "chunk": 1, 2 or 4
+// physical blocks at B = 32, 16, 8).  Lane roles (lane = 16 c + r, c in 0..3,
+// r in 0..15):
 //   QK^T   S^T[t][g] = sum_d K[t][d] Q[g][d] as two 16x16x32 MFMAs per 16-token
-//          half u of a 32-token chunk and per 32-wide slice of d.
+//          half u of the chunk and per 32-wide slice of d.
 //          A operand (K): lane (c, r) holds 8 dims [32 hs + 8 c, +8) of token
 //          tok(u, r) = 8 (r / 4) + 4 u + r % 4 (one 16-byte load).
 //          B operand (Q): lane (c, r) holds the same 8 dims of query head g = r
@@ -128,30 +155,502 @@ __device__ __forceinline__ void write_partition_result(const DecodeParams& prm, 
 // rows; every V load instruction covers whole 32-byte token runs of 16
 // feature rows of one or two tiles, so a chunk's loads touch only the bytes
 // of its blocks, each once.
+template <int D, int BS>
+struct Mfma {
+  static_assert(D % 32 == 0 && D <= 128, "head_dim");
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block_size");
+  static constexpr int HS = D / 32;                  // 32-wide slices of d (QK^T k-steps)
+  static constexpr int NT = D / 16;                  // 16-wide slices of d (P.V n-tiles)
+  static constexpr int NB = BS >= 32 ? 1 : 32 / BS;  // physical blocks per chunk
+  static constexpr size_t kTile = static_cast<size_t>(BS) * D;  // elements per (block, head)
+
+  struct Regs {  // one chunk's operands
+    bf16x8_t k[2][HS];
+    bf16x8_t v[NT];
+  };
+  struct State {  // online softmax of the G query heads of one KV head
+    float m2;        // running max of head g = r, base-2 units
+    f32x4_t acc[NT];
+    f32x4_t lsum;
+    __device__ void reset() {
+      m2 = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      lsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  struct Lane {  // lane-constant address parts
+    int kj[2], koff[2], vj, voff;
+    __device__ explicit Lane(int c, int r) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tok = 8 * (r >> 2) + 4 * u + (r & 3);
+        kj[u] = tok / BS;
+        koff[u] = (tok % BS) * D + 8 * c;
+      }
+      vj = (8 * c) / BS;
+      voff = r * BS + (8 * c) % BS;
+    }
+  };
+
+  // Query group of KV head `kvh` of sequence b as the QK^T B operand.
+  static __device__ void load_q(const uint16_t* q, int Hq, int G, int b, int kvh, int c, int r,
+                                bf16x8_t (&qop)[HS]) {
+    const uint16_t* qrow =
+        q + (static_cast<size_t>(b) * Hq + kvh * G + (r < G ? r : 0)) * D + 8 * c;
+#pragma unroll
+    for (int hs = 0; hs < HS; ++hs) qop[hs] = load_bf16x8(qrow + 32 * hs);
+    if (r >= G) {
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) qop[hs] = bf16x8_t{};
+    }
+  }
+
+  // Issues the loads of one chunk whose NB (block, head) tiles start at the
+  // element offsets `base` (wave-uniform).
+  static __device__ void load(const uint16_t* k_cache, const uint16_t* v_cache,
+                              const size_t (&base)[NB], const Lane& ln, Regs& x) {
+    auto pick = [&](int j) {
+      size_t v = base[0];
+#pragma unroll
+      for (int jj = 1; jj < NB; ++jj) v = (j == jj) ? base[jj] : v;
+      return v;
+    };
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint16_t* kp = k_cache + pick(ln.kj[u]) + ln.koff[u];
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) x.k[u][hs] = load_bf16x8(kp + 32 * hs);
+    }
+    const uint16_t* vp = v_cache + pick(ln.vj) + ln.voff;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) x.v[nt] = load_bf16x8(vp + 16 * nt * BS);
+  }
+
+  // Folds one chunk into the state.  Tokens valid .. 31 of the chunk
+  // (valid in 1..32, wave-uniform) lie past the sequence: their scores are
+  // selected to -inf and their V rows to 0, so whatever those slots hold
+  // (NaN included) never reaches the result.
+  static __device__ void step(const bf16x8_t (&qop)[HS], Regs& x, int valid, float sl, int c,
+                              State& st) {
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hs = 0; hs < HS; ++hs) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[0][hs], qop[hs], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[1][hs], qop[hs], s1, 0, 0, 0);
+    }
+    // xs[e]: score of token 8 c + e in base-2 units, e = 4 u + i
+    float xs[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xs[i] = s0[i] * sl;
+      xs[4 + i] = s1[i] * sl;
+    }
+    const bool tail = valid < 32;   // wave-uniform
+    const int lv = valid - 8 * c;   // tokens of this lane group still in range
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = (e < lv) ? xs[e] : -INFINITY;
+    }
+    float cm = xs[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, xs[e]);
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    // every lane of head g now holds the chunk maximum of head g
+    if (__ballot(cm > st.m2 + kRescaleThreshold) != 0) {
+      const float mn = fmaxf(st.m2, cm);
+      const float alpha = fast_exp2(st.m2 - mn);  // 0 on the first chunk (m2 = -inf)
+      st.m2 = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * c + i);  // factor of head 4 c + i
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st.acc[nt][i] *= a;
+        st.lsum[i] *= a;
+      }
+    }
+    bf16x8_t pa;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(fast_exp2(xs[e] - st.m2));
+    if (tail) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x.v[nt][e] = (e < lv) ? x.v[nt][e] : static_cast<__bf16>(0.f);
+    }
+    const bf16x8_t ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, x.v[nt], st.acc[nt], 0, 0, 0);
+    st.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, st.lsum, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Stream kernel.
 //
-// Latency: the sequence length, the partition's slice of the block table (one
-// entry per lane, at most 128 entries) and the query group are requested
-// together before anything waits; chunk addresses then come from the table
-// slice by lane reads, so no load in the streaming loop waits on another
-// load.  Each wave keeps kDepth chunks (8 KiB each at head_dim 64) in flight.
+// Work units are (sequence b, KV head h) in the order u = b Hkv + h; unit u
+// holds n_b = ceil(T_b / 32) chunks, and the C = Hkv sum_b n_b chunks of a
+// call are numbered in unit order.  Wavefront g of the W launched takes chunks
+// [g C / W', (g + 1) C / W') with W' = min(W, C), so every wavefront streams
+// the same number of bytes, to one chunk.  The stretch of a unit inside one
+// wavefront's range is a piece.  A piece that is a whole unit writes the
+// output directly.  Otherwise it publishes (acc, max, sum) into workspace slot
+// u + g (unique: ranges and units both advance with g, so two pieces with the
+// same u + g cannot exist), counts itself on the unit's counter and, if it is
+// the last of the unit's pieces (one per wavefront from the owner of the
+// unit's first chunk to the owner of its last), merges them all by the
+// rescaled segment rule into the output.
 //
-// Split-KV: a partition's result (unnormalised accumulator, maximum and
-// denominator) goes to the workspace; the last workgroup of a (sequence, KV
-// head) to finish - found with a counter that it returns to zero afterwards -
-// merges all partitions by the rescaled segment rule and writes the output, so
-// no second kernel runs.
+// Set-up: each workgroup puts the sequence lengths and the exclusive prefix
+// of chunk counts in LDS.  Each wavefront then takes its range in batches of
+// up to 64 chunks: lane i works out chunk i's unit, position in the unit,
+// valid token count and physical blocks (one table read each), and the
+// streaming loop reads these back by lane, with no memory access, kDepth
+// chunks ahead of the one it folds in.
+constexpr int kStreamWaves = 4;       // wavefronts per workgroup, each with its own range
+constexpr int kStreamMaxSeqs = 2048;  // sequences whose lengths and prefix fit in LDS
+
+template <int D, int BS>
+__global__ void __launch_bounds__(kStreamWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+    decode_stream(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+                  const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+                  const int32_t* __restrict__ seq_lens, const DecodeParams prm) {
+  using M = Mfma<D, BS>;
+  using Regs = typename M::Regs;
+  constexpr int NB = M::NB;
+  constexpr int HS = M::HS;
+  constexpr int NT = M::NT;
+  constexpr int DEPTH = kDepth;
+  constexpr int NTH = kStreamWaves * 64;
+  constexpr int kBlocksPerChunk = 32 / BS < 1 ? 1 : 32 / BS;
+  __shared__ int s_len[kStreamMaxSeqs];
+  __shared__ int s_pre[kStreamMaxSeqs + 1];
+  __shared__ int s_wsum[kStreamWaves];
+  constexpr int kMergeStage = 256;  // (max, sum) pairs a wavefront can stage for a merge
+  __shared__ float s_mrg[kStreamWaves][2 * kMergeStage];
+
+  const int S = prm.num_seqs;
+  const int Hkv = prm.num_kv_heads;
+  const int Hq = prm.num_q_heads;
+  const int G = prm.group;
+  const int MB = prm.max_blocks_per_seq;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane >> 4;
+  const int r = lane & 15;
+
+  // 1. Lengths, and the exclusive prefix of per-sequence chunk counts.
+  for (int b = tid; b < S; b += NTH) s_len[b] = seq_lens[b];
+  __syncthreads();
+  const int per = (S + NTH - 1) / NTH;  // thread tid sums sequences [tid per, tid per + per)
+  int mine = 0;
+  for (int j = 0; j < per; ++j) {
+    const int b = tid * per + j;
+    if (b < S) mine += (s_len[b] + 31) >> 5;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  for (int ww = 0; ww < w; ++ww) run += s_wsum[ww];
+  for (int j = 0; j < per; ++j) {
+    const int b = tid * per + j;
+    if (b < S) {
+      s_pre[b] = run;
+      run += (s_len[b] + 31) >> 5;
+    }
+  }
+  if (tid == NTH - 1) s_pre[S] = run;
+  __syncthreads();
+
+  // 2. Sequences with no tokens get a zero output row.
+  for (int b = blockIdx.x; b < S; b += gridDim.x)
+    if (s_len[b] == 0)
+      for (int e = tid; e < Hq * D; e += NTH)
+        store_out(prm.out, static_cast<size_t>(b) * Hq * D + e, 0.f, prm.out_f32);
+
+  // 3. This wavefront's share of the chunks.  (No barrier below this point:
+  // the wavefronts of a workgroup are independent from here on.)
+  const int64_t C = static_cast<int64_t>(Hkv) * s_pre[S];
+  const int64_t W = static_cast<int64_t>(gridDim.x) * kStreamWaves;
+  const int64_t Weff = C < W ? C : W;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kStreamWaves + w;
+  if (g >= Weff) return;
+  const int64_t start = g * C / Weff;
+  const int64_t end = (g + 1) * C / Weff;
+
+  const typename M::Lane ln(c, r);
+  const float sl = prm.scale_log2;
+  const size_t blk_stride = static_cast<size_t>(Hkv) * M::kTile;
+  typename M::State st;
+  st.reset();
+  bf16x8_t qop[HS];
+  int pb = 0, ph = 0, plc0 = 0;  // the piece being folded: sequence, KV head, first chunk
+
+  // Ends the current piece whose last chunk is `last_lc` of its unit.
+  auto finish_piece = [&](int last_lc) {
+    const int T = s_len[pb];
+    const int nb = (T + 31) >> 5;
+    const size_t row0 = static_cast<size_t>(pb) * Hq + static_cast<size_t>(ph) * G;
+    if (plc0 == 0 && last_lc == nb - 1) {  // the whole unit: final output
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gh = 4 * c + i;
+        if (gh < G) {
+          const float inv = 1.0f / st.lsum[i];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            store_out(prm.out, (row0 + gh) * D + 16 * nt + r, st.acc[nt][i] * inv, prm.out_f32);
+        }
+      }
+      return;
+    }
+    const int64_t u = static_cast<int64_t>(pb) * Hkv + ph;
+    float* pacc = prm.part_out + (u + g) * G * D;  // [G][D]
+    float* pml = prm.part_ml + (u + g) * G * 2;    // [G][max, sum]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int gh = 4 * c + i;
+      if (gh < G) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) store_coherent(pacc + gh * D + 16 * nt + r, st.acc[nt][i]);
+        if (r == 0) store_coherent(pml + gh * 2 + 1, st.lsum[i]);
+      }
+    }
+    if (c == 0 && r < G) store_coherent(pml + r * 2, st.m2);
+    // the stores are complete (visible chip-wide) before the count is made
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(prm.counters + u, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    const int64_t cu0 = static_cast<int64_t>(Hkv) * s_pre[pb] + static_cast<int64_t>(ph) * nb;
+    const int64_t gf = ((cu0 + 1) * Weff - 1) / C;   // owner of the unit's first chunk
+    const int64_t gl = ((cu0 + nb) * Weff - 1) / C;  // owner of its last chunk
+    if (prev != static_cast<uint32_t>(gl - gf)) return;
+    // Last piece: merge the unit's k pieces in wavefront order (so the result
+    // does not depend on which piece arrived last).  Their (max, sum) pairs
+    // go to this wavefront's LDS area, all loads in flight at once; then each
+    // lane folds four adjacent features of one head, sixteen pieces' loads at
+    // a time.
+    const int k = static_cast<int>(gl - gf + 1);
+    float* sm = s_mrg[w];
+    float* sq = s_mrg[w] + kMergeStage;
+    const bool staged = G * k <= kMergeStage;
+    if (staged) {
+      // the unit's k slots: acc [k][G][D] and (max, sum) [k][G][2]
+      const CoherentReader racc(prm.part_out + (u + gf) * G * D,
+                                static_cast<uint32_t>(k * G * D * sizeof(float)));
+      const CoherentReader rml(prm.part_ml + (u + gf) * G * 2,
+                               static_cast<uint32_t>(k * G * 2 * sizeof(float)));
+      // G * k <= 256: at most four (head, piece) pairs per lane, loaded first
+      float m4[4], l4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int idx = min(lane + 64 * t, G * k - 1);
+        const int gh = idx / k;
+        const int j = idx - gh * k;
+        const uint32_t off = static_cast<uint32_t>((j * G + gh) * 2 * sizeof(float));
+        m4[t] = rml.f32(off);
+        l4[t] = rml.f32(off + sizeof(float));
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int idx = lane + 64 * t;
+        if (idx < G * k) {
+          sm[idx] = m4[t];
+          sq[idx] = l4[t];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int e = lane; e < G * D / 4; e += 64) {
+        const int gh = (4 * e) / D;
+        const int d0 = 4 * e - gh * D;
+        float mx = -INFINITY;
+        for (int j = 0; j < k; ++j) mx = fmaxf(mx, sm[gh * k + j]);
+        float den = 0.f;
+        f32x4_t nm = {0.f, 0.f, 0.f, 0.f};
+        // eight pieces' accumulators in flight at a time
+        for (int j0 = 0; j0 < k; j0 += 8) {
+          f32x4_t a[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int j = min(j0 + t, k - 1);
+            a[t] = racc.f32x4(static_cast<uint32_t>(((j * G + gh) * D + d0) * sizeof(float)));
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            if (j0 + t < k) {
+              const float f = fast_exp2(sm[gh * k + j0 + t] - mx);
+              den += f * sq[gh * k + j0 + t];
+              nm += f * a[t];
+            }
+          }
+        }
+        const float inv = 1.0f / den;
+        const size_t o = (row0 + gh) * D + d0;
+        store_out(prm.out, o, nm[0] * inv, prm.out_f32);
+        store_out(prm.out, o + 1, nm[1] * inv, prm.out_f32);
+        store_out(prm.out, o + 2, nm[2] * inv, prm.out_f32);
+        store_out(prm.out, o + 3, nm[3] * inv, prm.out_f32);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gh = 4 * c + i;
+        if (gh < G) {
+          float mx = -INFINITY, den = 0.f, num[NT];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) num[nt] = 0.f;
+          for (int64_t gg = gf; gg <= gl; ++gg) {
+            const float* oml = prm.part_ml + ((u + gg) * G + gh) * 2;
+            const float* oacc = prm.part_out + ((u + gg) * G + gh) * D + r;
+            const float mj = load_coherent(oml);
+            const float lj = load_coherent(oml + 1);
+            const float mn = fmaxf(mx, mj);
+            const float fo = fast_exp2(mx - mn);  // 0 for the first piece
+            const float fj = fast_exp2(mj - mn);
+            den = den * fo + lj * fj;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              num[nt] = num[nt] * fo + load_coherent(oacc + 16 * nt) * fj;
+            mx = mn;
+          }
+          const float inv = 1.0f / den;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            store_out(prm.out, (row0 + gh) * D + 16 * nt + r, num[nt] * inv, prm.out_f32);
+        }
+      }
+    }
+    // every piece has been counted: leave the counter at zero for the next call
+    if (lane == 0)
+      __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  for (int64_t bat = start; bat < end; bat += 64) {
+    const int n = static_cast<int>(end - bat < 64 ? end - bat : 64);
+    // Lane i describes chunk bat + i: sequence, KV head, chunk of the unit,
+    // valid tokens, piece start / end flags and physical blocks.
+    int cb = 0, chd = 0, clc = 0, cval = 0, cfl = 0;
+    int ent[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) ent[j] = 0;
+    if (lane < n) {
+      const int64_t cc = bat + lane;
+      int lo = 0, hi = S;  // largest lo with Hkv * s_pre[lo] <= cc
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (static_cast<int64_t>(Hkv) * s_pre[mid] <= cc)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      const int T = s_len[lo];
+      const int nb = (T + 31) >> 5;
+      const int rem = static_cast<int>(cc - static_cast<int64_t>(Hkv) * s_pre[lo]);
+      cb = lo;
+      chd = rem / nb;
+      clc = rem - chd * nb;
+      cval = min(32, T - 32 * clc);
+      cfl = ((cc == start || clc == 0) ? 1 : 0) | ((cc == end - 1 || clc == nb - 1) ? 2 : 0);
+      const int last_blk = (T + BS - 1) / BS - 1;
+      const int32_t* row = block_tables + static_cast<size_t>(lo) * MB;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) ent[j] = row[min(clc * kBlocksPerChunk + j, last_blk)];
+    }
+
+    auto issue = [&](int i, Regs& x) {
+      const size_t head_off = static_cast<size_t>(__builtin_amdgcn_readlane(chd, i)) * M::kTile;
+      size_t base[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        base[j] = static_cast<size_t>(__builtin_amdgcn_readlane(ent[j], i)) * blk_stride + head_off;
+      M::load(k_cache, v_cache, base, ln, x);
+    };
+    auto consume = [&](int i, Regs& x) {
+      const int fl = __builtin_amdgcn_readlane(cfl, i);
+      if (fl & 1) {  // a piece starts: its query group, a fresh state
+        pb = __builtin_amdgcn_readlane(cb, i);
+        ph = __builtin_amdgcn_readlane(chd, i);
+        plc0 = __builtin_amdgcn_readlane(clc, i);
+        st.reset();
+        M::load_q(q, Hq, G, pb, ph, c, r, qop);
+        // wait for the query here, inside the branch: the wait counts after
+        // the join then stay those of the chunk ring
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      M::step(qop, x, __builtin_amdgcn_readlane(cval, i), sl, c, st);
+      if (fl & 2) finish_piece(__builtin_amdgcn_readlane(clc, i));
+    };
+
+    // Ring of DEPTH chunks in flight; the steady-state refills are
+    // unconditional so the wait counts stay exact, only the drain is not.
+    Regs ring[DEPTH];
+    if (n >= DEPTH) {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) issue(s, ring[s]);
+      int i = 0;
+      for (; i + 2 * DEPTH - 1 < n; i += DEPTH) {
+#pragma unroll
+        for (int s = 0; s < DEPTH; ++s) {
+          consume(i + s, ring[s]);
+          issue(i + s + DEPTH, ring[s]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) {
+        consume(i + s, ring[s]);
+        if (i + s + DEPTH < n) issue(i + s + DEPTH, ring[s]);
+      }
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s)
+        if (i + s + DEPTH < n) consume(i + s + DEPTH, ring[s]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s)
+        if (s < n) issue(s, ring[s]);
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s)
+        if (s < n) consume(s, ring[s]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Partitioned kernel.
+//
+// One workgroup per (partition, KV head, sequence); its NW wavefronts take the
+// partition's chunks round robin (wave w: chunks w, w + NW, ...) and merge
+// through LDS.  Partitions hold partition_size tokens (a sequence's last one
+// fewer), or - balanced - share the sequence's chunks evenly.  The
+// partition's slice of the block table (at most 128 entries) is read with one
+// load per lane and looked up by lane reads.  A split sequence's partitions
+// publish (acc, max, sum) to the workspace and count themselves on the
+// (sequence, KV head) counter; the last to arrive merges them all.
 template <int D, int BS, int NW>
 __global__ void __launch_bounds__(NW * 64)
     decode_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                 const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                 const int32_t* __restrict__ seq_lens, const DecodeParams prm) {
-  static_assert(D % 32 == 0 && D <= 128, "head_dim");
-  static_assert(BS == 8 || BS == 16 || BS == 32, "block_size");
-  constexpr int HS = D / 32;                  // 32-wide slices of d (QK^T k-steps)
-  constexpr int NT = D / 16;                  // 16-wide slices of d (P.V n-tiles)
-  constexpr int NB = BS >= 32 ? 1 : 32 / BS;  // physical blocks per 32-token chunk
+  using M = Mfma<D, BS>;
+  using Regs = typename M::Regs;
+  constexpr int NB = M::NB;
+  constexpr int HS = M::HS;
+  constexpr int NT = M::NT;
   constexpr int DEPTH = kDepth;
-  constexpr size_t kTile = static_cast<size_t>(BS) * D;  // elements per (block, head) tile
 
   __shared__ float s_m[NW][16];
   __shared__ float s_l[NW][16];
@@ -167,6 +666,7 @@ __global__ void __launch_bounds__(NW * 64)
   const int r = lane & 15;
   const int G = prm.group;
   const int Hkv = prm.num_kv_heads;
+  const int Hq = prm.num_q_heads;
   const int PS = prm.partition_size;
   const int MB = prm.max_blocks_per_seq;
   const bool balanced = prm.balanced != 0;
@@ -174,59 +674,35 @@ __global__ void __launch_bounds__(NW * 64)
 
   // The partition's slice of the block table, one entry per lane (<= 128).
   int tb0 = 0, tb1 = 0;
-  auto load_slice = [&](int lb0, int n) {
-    if (lane < n && lb0 + lane < MB) tb0 = btrow[lb0 + lane];
-    if (lane + 64 < n && lb0 + lane + 64 < MB) tb1 = btrow[lb0 + lane + 64];
+  auto load_slice = [&](int lb0, int cnt) {
+    if (lane < cnt && lb0 + lane < MB) tb0 = btrow[lb0 + lane];
+    if (lane + 64 < cnt && lb0 + lane + 64 < MB) tb1 = btrow[lb0 + lane + 64];
   };
   // Fixed-size partitions: the slice, the query group and the length are
   // requested together before anything waits.
   if (!balanced) load_slice(p * (PS / BS), PS / BS);
   bf16x8_t qop[HS];
-  {
-    const uint16_t* qrow =
-        q + (static_cast<size_t>(b) * prm.num_q_heads + h * G + (r < G ? r : 0)) * D + 8 * c;
-#pragma unroll
-    for (int hs = 0; hs < HS; ++hs) qop[hs] = load_bf16x8(qrow + 32 * hs);
-    if (r >= G) {
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) qop[hs] = bf16x8_t{};
-    }
-  }
+  M::load_q(q, Hq, G, b, h, c, r, qop);
   const int T = seq_lens[b];
   const int nparts = (T + PS - 1) / PS;
   if (p >= (nparts > 0 ? nparts : 1)) return;
 
   // Balanced partitions: the sequence's ceil(T / 32) chunks are dealt out
-  // evenly over its nparts partitions (each then holds at most PS tokens), so
-  // no workgroup is left with a short remainder while others run long.
+  // evenly over its nparts partitions (each then holds at most PS tokens).
   const int part_len =
       (balanced && nparts > 0) ? 32 * ((((T + 31) >> 5) + nparts - 1) / nparts) : PS;
   const int t_begin = p * part_len;
   const int t_end = min(t_begin + part_len, T);
   if (balanced) load_slice(t_begin / BS, part_len / BS);
-  const int span = t_end - t_begin;             // tokens of this partition (0 only if T == 0)
-  const int nch = (span + 31) >> 5;             // 32-token chunks
+  const int span = t_end - t_begin;               // tokens of this partition (0 only if T == 0)
+  const int nch = (span + 31) >> 5;               // 32-token chunks
   const int last_blk = (span + BS - 1) / BS - 1;  // last table entry of the slice in use
   const float sl = prm.scale_log2;
-  const size_t head_off = static_cast<size_t>(h) * kTile;
-  const size_t blk_stride = static_cast<size_t>(Hkv) * kTile;
-
-  float m2 = -INFINITY;  // running max of head g = r, base-2 units
-  f32x4_t acc[NT];
-  f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // lane-constant parts of the addresses
-  int kj[2], koff[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int tok = 8 * (r >> 2) + 4 * u + (r & 3);
-    kj[u] = tok / BS;
-    koff[u] = (tok % BS) * D + 8 * c;
-  }
-  const int vj = (8 * c) / BS;
-  const int voff = r * BS + (8 * c) % BS;
+  const size_t head_off = static_cast<size_t>(h) * M::kTile;
+  const size_t blk_stride = static_cast<size_t>(Hkv) * M::kTile;
+  const typename M::Lane ln(c, r);
+  typename M::State st;
+  st.reset();
 
   // Physical block of partition-relative block lb (uniform).  Entries past
   // the last one holding tokens are never used: the index is clamped to it,
@@ -236,136 +712,63 @@ __global__ void __launch_bounds__(NW * 64)
     lb = min(lb, last_blk);
     return lb < 64 ? __builtin_amdgcn_readlane(tb0, lb) : __builtin_amdgcn_readlane(tb1, lb - 64);
   };
-  auto load_chunk = [&](int k, bf16x8_t (&kr)[2][HS], bf16x8_t (&vr)[NT]) {
+  auto issue = [&](int k, Regs& x) {
     const int lbc = (32 * k) / BS;
     size_t base[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       base[j] = static_cast<size_t>(entry(lbc + j)) * blk_stride + head_off;
-    auto pick = [&](int j) {
-      size_t v = base[0];
-#pragma unroll
-      for (int jj = 1; jj < NB; ++jj) v = (j == jj) ? base[jj] : v;
-      return v;
-    };
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint16_t* kp = k_cache + pick(kj[u]) + koff[u];
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) kr[u][hs] = load_bf16x8(kp + 32 * hs);
-    }
-    const uint16_t* vp = v_cache + pick(vj) + voff;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) vr[nt] = load_bf16x8(vp + 16 * nt * BS);
+    M::load(k_cache, v_cache, base, ln, x);
   };
+  auto consume = [&](int k, Regs& x) { M::step(qop, x, min(32, span - 32 * k), sl, c, st); };
 
-  const bf16x8_t ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-  auto process_chunk = [&](int k, bf16x8_t (&kr)[2][HS], bf16x8_t (&vr)[NT]) {
-    const int t = 32 * k;  // partition-relative
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int hs = 0; hs < HS; ++hs) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[0][hs], qop[hs], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[1][hs], qop[hs], s1, 0, 0, 0);
-    }
-    // x[e]: score of token t + 8 c + e in base-2 units, e = 4 u + i
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = s0[i] * sl;
-      x[4 + i] = s1[i] * sl;
-    }
-    const bool tail = t + 32 > span;  // wave-uniform
-    const int valid = span - t - 8 * c;  // tokens of this lane group still in range
-    if (tail) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (e < valid) ? x[e] : -INFINITY;
-    }
-    float cm = x[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
-    // every lane of head g now holds the chunk maximum of head g
-    if (__ballot(cm > m2 + kRescaleThreshold) != 0) {
-      const float mn = fmaxf(m2, cm);
-      const float alpha = fast_exp2(m2 - mn);  // 0 on the first chunk (m2 = -inf)
-      m2 = mn;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = __shfl(alpha, 4 * c + i);  // factor of head 4 c + i
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][i] *= a;
-        lsum[i] *= a;
-      }
-    }
-    bf16x8_t pa;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(fast_exp2(x[e] - m2));
-    if (tail) {
-      // V rows of tokens >= T may hold anything (NaN included): select 0
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          vr[nt][e] = (e < valid) ? vr[nt][e] : static_cast<__bf16>(0.f);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vr[nt], acc[nt], 0, 0, 0);
-    lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, lsum, 0, 0, 0);
-  };
-
-  // Software pipeline over this wave's chunks w, w + NW, ...: ring slot s
-  // holds chunk i with i % DEPTH == s and is refilled with chunk i + DEPTH as
-  // soon as chunk i has been consumed.  In the steady-state loop every refill
-  // is unconditional, so the compiler's wait counts stay exact (each wait
-  // leaves the younger DEPTH - 1 chunks in flight); only the final drain has
-  // conditional refills.
+  // Ring over this wave's chunks w, w + NW, ...: slot s holds chunk i with
+  // i % DEPTH == s and is refilled with chunk i + DEPTH as soon as chunk i has
+  // been consumed.  Steady-state refills are unconditional, so the compiler's
+  // wait counts stay exact; only the drain has conditional refills.
   const int my_n = w < nch ? (nch - 1 - w) / NW + 1 : 0;
-  bf16x8_t kr[DEPTH][2][HS], vr[DEPTH][NT];
+  Regs ring[DEPTH];
   if (my_n >= DEPTH) {
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) load_chunk(w + NW * s, kr[s], vr[s]);
+    for (int s = 0; s < DEPTH; ++s) issue(w + NW * s, ring[s]);
     int i = 0;
     for (; i + 2 * DEPTH - 1 < my_n; i += DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; ++s) {
-        process_chunk(w + NW * (i + s), kr[s], vr[s]);
-        load_chunk(w + NW * (i + s + DEPTH), kr[s], vr[s]);
+        consume(w + NW * (i + s), ring[s]);
+        issue(w + NW * (i + s + DEPTH), ring[s]);
       }
     }
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s) {
-      process_chunk(w + NW * (i + s), kr[s], vr[s]);
-      if (i + s + DEPTH < my_n) load_chunk(w + NW * (i + s + DEPTH), kr[s], vr[s]);
+      consume(w + NW * (i + s), ring[s]);
+      if (i + s + DEPTH < my_n) issue(w + NW * (i + s + DEPTH), ring[s]);
     }
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s)
-      if (i + s + DEPTH < my_n) process_chunk(w + NW * (i + s + DEPTH), kr[s], vr[s]);
+      if (i + s + DEPTH < my_n) consume(w + NW * (i + s + DEPTH), ring[s]);
   } else {
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s)
-      if (s < my_n) load_chunk(w + NW * s, kr[s], vr[s]);
+      if (s < my_n) issue(w + NW * s, ring[s]);
 #pragma unroll
     for (int s = 0; s < DEPTH; ++s)
-      if (s < my_n) process_chunk(w + NW * s, kr[s], vr[s]);
+      if (s < my_n) consume(w + NW * s, ring[s]);
   }
 
   // Merge the wavefronts' (m, l, acc) in LDS by the rescaled segment rule.
-  if (c == 0) s_m[w][r] = m2;
+  if (c == 0) s_m[w][r] = st.m2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int g = 4 * c + i;
     if (g < G) {
-      if (r == 0) s_l[w][g] = lsum[i];
+      if (r == 0) s_l[w][g] = st.lsum[i];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s_acc[w][g][16 * nt + r] = acc[nt][i];
+      for (int nt = 0; nt < NT; ++nt) s_acc[w][g][16 * nt + r] = st.acc[nt][i];
     }
   }
   __syncthreads();
   const bool split = nparts > 1;
-  const int Hq = prm.num_q_heads;
   const int NP = prm.num_partitions;
   for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
     const int g = idx / D;
@@ -420,8 +823,10 @@ __global__ void __launch_bounds__(NW * 64)
       const int g = idx / nparts;
       const int pp = idx - g * nparts;
       const size_t row = static_cast<size_t>(b) * Hq + h * G + g;
-      s_pm[idx] = load_coherent(prm.part_ml + (row * NP + pp) * 2);
-      s_pm[kStage + idx] = load_coherent(prm.part_ml + (row * NP + pp) * 2 + 1);
+      const CoherentReader rml(prm.part_ml + row * NP * 2,
+                               static_cast<uint32_t>(NP * 2 * sizeof(float)));
+      s_pm[idx] = rml.f32(static_cast<uint32_t>(pp * 2 * sizeof(float)));
+      s_pm[kStage + idx] = rml.f32(static_cast<uint32_t>((pp * 2 + 1) * sizeof(float)));
     }
   }
   __syncthreads();
@@ -434,12 +839,25 @@ __global__ void __launch_bounds__(NW * 64)
     if (staged) {
       const float* pm = s_pm + g * nparts;
       const float* pl = s_pm + kStage + g * nparts;
+      const CoherentReader racc(prm.part_out + row * NP * D,
+                                static_cast<uint32_t>(NP * D * sizeof(float)));
       for (int pp = 0; pp < nparts; ++pp) mx = fmaxf(mx, pm[pp]);
-#pragma unroll 16
-      for (int pp = 0; pp < nparts; ++pp) {
-        const float f = fast_exp2(pm[pp] - mx);
-        num += f * load_coherent(po + static_cast<size_t>(pp) * D);
-        den += f * pl[pp];
+      // eight partitions' accumulators in flight at a time
+      for (int p0 = 0; p0 < nparts; p0 += 8) {
+        float a[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int pp = min(p0 + t, nparts - 1);
+          a[t] = racc.f32(static_cast<uint32_t>((pp * D + d) * sizeof(float)));
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if (p0 + t < nparts) {
+            const float f = fast_exp2(pm[p0 + t] - mx);
+            num += f * a[t];
+            den += f * pl[p0 + t];
+          }
+        }
       }
     } else {
       const float* ml = prm.part_ml + row * NP * 2;
@@ -597,6 +1015,26 @@ hipError_t launch_mfma_bs(const DecodeLaunch& a, int waves, dim3 grid, hipStream
   }
 }
 
+template <int D>
+hipError_t launch_stream_bs(const DecodeLaunch& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kStreamWaves * 64);
+  switch (a.prm.block_size) {
+    case 8:
+      decode_stream<D, 8><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache, a.block_tables,
+                                                      a.seq_lens, a.prm);
+      break;
+    case 16:
+      decode_stream<D, 16><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache, a.block_tables,
+                                                       a.seq_lens, a.prm);
+      break;
+    default:
+      decode_stream<D, 32><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache, a.block_tables,
+                                                       a.seq_lens, a.prm);
+      break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_merge_for(const DecodeLaunch& a, hipStream_t stream) {
   const DecodeParams& prm = a.prm;
   return launch_merge(prm.part_out, prm.part_lse, a.num_seqs * prm.num_q_heads,
@@ -613,6 +1051,14 @@ bool mfma_shape_supported(int head_dim, int block_size, int group, int partition
          partition_size / block_size <= 128;
 }
 
+bool stream_shape_supported(int head_dim, int block_size, int group, int num_seqs) {
+  return (head_dim == 64 || head_dim == 128) &&
+         (block_size == 8 || block_size == 16 || block_size == 32) && group >= 1 &&
+         group <= 16 && num_seqs <= kStreamMaxSeqs;
+}
+
+int stream_waves_per_group() { return kStreamWaves; }
+
 bool generic_shape_supported(int head_dim, int block_size, int group) {
   return head_dim >= 1 && head_dim <= 256 && block_size >= 1 && group >= 1;
 }
@@ -621,6 +1067,12 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, int waves, hipStream_t stre
   const dim3 grid(a.prm.num_partitions, a.prm.num_kv_heads, a.num_seqs);
   return (a.prm.head_dim == 64) ? launch_mfma_bs<64>(a, waves, grid, stream)
                                 : launch_mfma_bs<128>(a, waves, grid, stream);
+}
+
+hipError_t launch_decode_stream(const DecodeLaunch& a, int num_waves, hipStream_t stream) {
+  const dim3 grid(num_waves / kStreamWaves);
+  return (a.prm.head_dim == 64) ? launch_stream_bs<64>(a, grid, stream)
+                                : launch_stream_bs<128>(a, grid, stream);
 }
 
 hipError_t launch_decode_generic(const DecodeLaunch& a, hipStream_t stream) {

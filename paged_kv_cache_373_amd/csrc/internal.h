@@ -10,6 +10,7 @@ namespace pkv {
 
 // Everything a decode kernel needs besides the tensor pointers.
 struct DecodeParams {
+  int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;              // num_q_heads / num_kv_heads
@@ -22,7 +23,9 @@ struct DecodeParams {
   float scale_log2;           // scale * log2(e): scores live in base-2 units inside the kernels
   int32_t out_f32;            // 1: out is fp32, 0: out is bf16
   void* out;                  // [S, Hq, D]
-  // Split-KV workspace (only when num_partitions > 1).
+  // Split-KV workspace.  Partitioned kernels (only when num_partitions > 1):
+  // partition results per (sequence, q head, partition).  Stream kernel: one
+  // slot of G heads per piece, [S * Hkv + waves] slots.
   float* part_out;            // [S, Hq, num_partitions, D] partition outputs
   float* part_lse;            // [S, Hq, num_partitions] ln Z_r (vector kernel)
   float* part_ml;             // [S, Hq, num_partitions, 2] (max in base-2 units, sum)
@@ -41,11 +44,14 @@ struct DecodeLaunch {
   DecodeParams prm;
 };
 
-// Shapes the matrix-core kernel is instantiated for.
+// Shapes the kernels are instantiated for.
 bool mfma_shape_supported(int head_dim, int block_size, int group, int partition_size);
+bool stream_shape_supported(int head_dim, int block_size, int group, int num_seqs);
 bool generic_shape_supported(int head_dim, int block_size, int group);
+int stream_waves_per_group();  // the stream kernel's wavefronts per workgroup
 
 // Each launcher enqueues its kernel(s) on `stream` and returns the launch error.
+hipError_t launch_decode_stream(const DecodeLaunch& a, int num_waves, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeLaunch& a, int waves, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeLaunch& a, hipStream_t stream);
 

@@ -85,7 +85,7 @@ class GpuSide:
         w = self.w
         out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=out_dtype, device=DEV)
         kw.setdefault("max_seq_len", int(w.seq_lens.max(initial=0)))
-        if kw.get("partition_size", 0) == 0 and w.partition_size:
+        if "partition_size" not in kw and w.partition_size:
             kw["partition_size"] = w.partition_size
         pkv.paged_attention_decode(self.q, self.kc, self.vc, self.bt, self.lens, w.block_size,
                                    w.scale, out, **kw)

@@ -54,7 +54,7 @@ def test_header_compiles_as_c():
 
 
 def test_struct_layout_matches_binding():
-    assert ctypes.sizeof(pkv.DecodeDims) == 12 * 4
+    assert ctypes.sizeof(pkv.DecodeDims) == 13 * 4
 
 
 def test_version_and_status_strings():
@@ -67,7 +67,7 @@ def test_version_and_status_strings():
 def _dims(**kw):
     d = dict(num_seqs=2, num_q_heads=32, num_kv_heads=8, head_dim=64, num_blocks=10,
              max_blocks_per_seq=4, max_seq_len=64, partition_size=0, out_dtype=0, kernel=0,
-             waves_per_group=0, balance_partitions=0)
+             waves_per_group=0, balance_partitions=0, stream_waves=0)
     d.update(kw)
     return pkv.DecodeDims(**d)
 
@@ -79,17 +79,21 @@ def ws(dims, bs=16):
 BAD = ctypes.c_size_t(-1).value
 
 
-def test_workspace_size_rules():
-    assert ws(_dims()) == 0  # 64 tokens fit one 256-token partition
-    d = _dims(max_seq_len=64, partition_size=32)
+def zb(dims, bs=16):
+    return pkv.lib().pkv_decode_workspace_zeroed_bytes(ctypes.byref(dims), bs)
+
+
+def test_workspace_size_rules_partitioned():
+    m = dict(kernel=1)  # the partitioned matrix-core kernel
+    assert ws(_dims(**m)) == 0  # 64 tokens fit one 256-token partition
+    d = _dims(max_seq_len=64, partition_size=32, **m)
     # 2 partitions: counters [2*8] u32, outputs [2*32*2*64] fp32 and (max, sum)
     # pairs [2*32*2*2] fp32, each region rounded up to 256 bytes
     assert ws(d) == 256 + 2 * 32 * 2 * 64 * 4 + 2 * 32 * 2 * 2 * 4
-    assert pkv.lib().pkv_decode_workspace_zeroed_bytes(ctypes.byref(d), 16) == 256
-    assert pkv.lib().pkv_decode_workspace_zeroed_bytes(ctypes.byref(_dims()), 16) == 0
-    big = _dims(num_seqs=100, max_seq_len=64, partition_size=32)
-    assert pkv.lib().pkv_decode_workspace_zeroed_bytes(ctypes.byref(big), 16) == 3328  # 3200 -> 256k
-    assert ws(_dims(balance_partitions=2)) == BAD
+    assert zb(d) == 256
+    assert zb(_dims(**m)) == 0
+    big = _dims(num_seqs=100, max_seq_len=64, partition_size=32, **m)
+    assert zb(big) == 3328  # 800 counters = 3200 bytes, rounded up to 256
     assert ws(_dims(num_q_heads=30)) == BAD  # Hq % Hkv != 0
     assert ws(_dims(max_seq_len=65)) == BAD  # longer than the table holds
     assert ws(_dims(partition_size=24)) == BAD  # not a multiple of B
@@ -98,6 +102,23 @@ def test_workspace_size_rules():
     assert ws(_dims(kernel=2, head_dim=80)) == 0
     assert ws(_dims(waves_per_group=3)) == BAD
     assert ws(_dims(num_seqs=70000)) == BAD
+    assert ws(_dims(balance_partitions=2)) == BAD
+
+
+def test_workspace_size_rules_stream():
+    # 2 sequences x 8 KV heads, up to 64 tokens = 2 chunks each: 32 chunks at
+    # most, 4 per wavefront -> 8 wavefronts; slots = 16 units + 8 pieces
+    d = _dims(kernel=3)
+    slots = 16 + 8
+    assert ws(d) == 256 + slots * 4 * 64 * 4 + slots * 4 * 2 * 4
+    assert zb(d) == 256
+    assert ws(_dims()) == ws(d)  # AUTO with no partition size runs the stream kernel
+    d2 = _dims(kernel=3, stream_waves=64)
+    assert ws(d2) == 256 + (16 + 64) * 4 * 64 * 4 + (16 + 64) * 4 * 2 * 4
+    assert ws(_dims(kernel=3, stream_waves=6)) == BAD  # not a multiple of 4
+    assert ws(_dims(kernel=3, num_seqs=4096)) == BAD  # over the stream kernel's sequence limit
+    assert ws(_dims(num_seqs=4096)) == 0  # AUTO falls back to one 256-token partition
+    assert ws(_dims(kernel=3, head_dim=80)) == BAD
 
 
 def test_decode_rejects_before_any_hip_call():
@@ -116,6 +137,7 @@ def test_decode_rejects_before_any_hip_call():
     assert call(dims=ctypes.byref(bad)) == pkv.PKV_ERR_UNSUPPORTED
     split = _dims(max_seq_len=64, partition_size=32)
     assert call(dims=ctypes.byref(split)) == pkv.PKV_ERR_WORKSPACE  # no workspace given
+    assert call(dims=ctypes.byref(_dims())) == pkv.PKV_ERR_WORKSPACE  # stream kernel needs one
     empty = _dims(num_seqs=0)
     assert call(dims=ctypes.byref(empty)) == pkv.PKV_OK  # nothing to do
 

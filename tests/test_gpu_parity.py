@@ -50,17 +50,57 @@ def test_reshape_and_cache_bit_exact(name):
     _check_caches(GpuSide(w), OracleSide(w), name)
 
 
+def matrix_core_shape(w) -> bool:
+    g = w.num_q_heads // w.num_kv_heads
+    return w.head_dim in (64, 128) and w.block_size in (8, 16, 32) and g <= 16
+
+
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("kernel", ["auto", "generic"])
+@pytest.mark.parametrize("kernel", ["auto", "stream", "mfma", "generic"])
 def test_decode_small(name, kernel):
     say(f"case decode {name} kernel={kernel}")
     w = SMALL[name]()
+    if kernel in ("stream", "mfma") and not matrix_core_shape(w):
+        pytest.skip("shape outside the matrix-core kernels")
     g, o = GpuSide(w), OracleSide(w)
     ref = o.decode()
-    out = g.decode(torch.float32, kernel=kernel)
+    kw = dict(kernel=kernel)
+    if kernel == "mfma":
+        kw["partition_size"] = 64
+    out = g.decode(torch.float32, **kw)
     compare(out.cpu().numpy(), ref, strict_abs=True, what=f"{name}/{kernel}/f32")
-    outb = g.decode(torch.bfloat16, kernel=kernel)
+    outb = g.decode(torch.bfloat16, **kw)
     compare(outb.float().cpu().numpy(), ref, strict_abs=False, what=f"{name}/{kernel}/bf16")
+
+
+@pytest.mark.parametrize("waves", [4, 8, 12, 64, 256, 2048])
+def test_stream_wave_counts(waves):
+    """Fewer wavefronts than chunks (ranges over 64 chunks: several batches
+    per wavefront), more wavefronts than chunks (one chunk each), units cut
+    into many pieces; lengths include 0 and 1."""
+    say(f"case stream waves={waves}")
+    w = workloads.random_small(35, 9, 16, 4, 64, 16, 2100, min_len=0)
+    w.seq_lens[2] = 0
+    w.seq_lens[5] = 1
+    w.k_tok = w.k_tok[: int(w.seq_lens.sum())]
+    w.v_tok = w.v_tok[: int(w.seq_lens.sum())]
+    g, o = GpuSide(w), OracleSide(w)
+    ref = o.decode()
+    out = g.decode(torch.float32, kernel="stream", stream_waves=waves)
+    assert np.all(out[2].cpu().numpy() == 0)
+    compare(out.cpu().numpy(), ref, strict_abs=True, what=f"stream w{waves}")
+
+
+@pytest.mark.parametrize("num_seqs", [2048, 2100])
+def test_many_short_sequences(num_seqs):
+    """The stream kernel keeps every length in LDS up to 2048 sequences;
+    beyond that AUTO runs the partitioned kernel."""
+    say(f"case many sequences S={num_seqs}")
+    w = workloads.random_small(36, num_seqs, 8, 2, 64, 16, 40, min_len=0)
+    g, o = GpuSide(w), OracleSide(w)
+    ref = o.decode()
+    out = g.decode(torch.float32)
+    compare(out.cpu().numpy(), ref, strict_abs=True, what=f"S{num_seqs} auto")
 
 
 @pytest.mark.parametrize("ps", [32, 64, 96, 256, 512, 1024])
@@ -113,22 +153,29 @@ def test_edge_lengths():
             out = g.decode(torch.float32, kernel=kernel, partition_size=ps).cpu().numpy()
             assert np.all(out[0] == 0)
             compare(out, ref, strict_abs=True, what=f"edges {kernel} ps{ps}")
+    for waves in (4, 16, 400):
+        out = g.decode(torch.float32, kernel="stream", stream_waves=waves).cpu().numpy()
+        assert np.all(out[0] == 0)
+        compare(out, ref, strict_abs=True, what=f"edges stream w{waves}")
     # T = 1: the output is v_0 exactly (one weight of exactly 1)
-    out = g.decode(torch.float32).cpu().numpy()
     v0 = oracle.widen_bf16(w2.v_tok[0])  # sequence 1's only token (sequence 0 is empty)
-    np.testing.assert_array_equal(out[1], np.repeat(v0, 4, axis=0))
+    for kernel in ("stream", "mfma", "generic"):
+        out = g.decode(torch.float32, kernel=kernel).cpu().numpy()
+        np.testing.assert_array_equal(out[1], np.repeat(v0, 4, axis=0))
 
 
-def test_permutation_invariance_and_determinism():
-    say("case permutation invariance")
+@pytest.mark.parametrize("kernel", ["stream", "mfma"])
+def test_permutation_invariance_and_determinism(kernel):
+    say(f"case permutation invariance {kernel}")
     w = workloads.random_small(33, 6, 16, 4, 64, 16, 700)
     g = GpuSide(w)
-    a = g.decode(torch.float32).cpu()
-    b = g.decode(torch.float32).cpu()
+    kw = dict(kernel=kernel, partition_size=0 if kernel == "stream" else 128)
+    a = g.decode(torch.float32, **kw).cpu()
+    b = g.decode(torch.float32, **kw).cpu()
     assert torch.equal(a, b), "repeated runs differ"
     perm = workloads.rng(100, 78).permutation(w.num_blocks).astype(np.int32)
     g2 = GpuSide(w, block_tables=perm[w.block_tables])
-    c = g2.decode(torch.float32).cpu()
+    c = g2.decode(torch.float32, **kw).cpu()
     assert torch.equal(a, c), "output depends on physical placement"
 
 
@@ -209,15 +256,16 @@ def test_workspace_reuse_across_shapes():
     for rnd in range(3):
         for i, (gs, _) in enumerate(sides):
             for label, ws in (("tracked", tracked), ("raw", raw)):
-                for balanced in (False, True):
-                    out = gs.decode(torch.float32, partition_size=64, workspace=ws,
-                                    balance_partitions=balanced)
+                for kw in (dict(kernel="mfma", partition_size=64),
+                           dict(kernel="mfma", partition_size=64, balance_partitions=True),
+                           dict(kernel="stream", stream_waves=32)):
+                    out = gs.decode(torch.float32, workspace=ws, **kw)
                     compare(out.cpu().numpy(), refs[i], strict_abs=True,
-                            what=f"ws {label} round {rnd} case {i} balanced={balanced}")
+                            what=f"ws {label} round {rnd} case {i} {kw}")
     # every counter region a call used is zero again afterwards
     for i, (gs, _) in enumerate(sides):
         w = gs.w
-        dims = pkv._dims(gs.q, gs.kc, gs.bt, int(w.seq_lens.max()), 64, torch.float32, "auto", 0,
+        dims = pkv._dims(gs.q, gs.kc, gs.bt, int(w.seq_lens.max()), 64, torch.float32, "mfma", 0,
                          False)
         z = pkv.lib().pkv_decode_workspace_zeroed_bytes(pkv.ctypes.byref(dims), w.block_size)
         assert int(raw[:z].count_nonzero()) == 0
