@@ -1,11 +1,13 @@
 """Benchmark of the paged decode-attention hot path on one MI355X.
 
-One step = one decode step of one layer of the Llama-3.2-1B-shaped batch:
-``reshape_and_cache`` writes the new token of each of the 64 sequences into
-its slot, then ``paged_attention_decode`` attends over every cached token
-(32 q heads / 8 KV heads, head_dim 64, bf16, B = 16, lengths U[128, 2048],
-physical blocks a seeded permutation).  There is no copy-on-write in this
-workload (``copy_blocks`` has no pairs).
+One step = one decode step of one layer of the Llama-3.2-1B-shaped batch: the
+new token of each of the 64 sequences is written into its slot and attention
+runs over every cached token (32 q heads / 8 KV heads, head_dim 64, bf16,
+B = 16, lengths U[128, 2048], physical blocks a seeded permutation).  By
+default the step is one ``paged_attention_decode_append`` launch (write and
+attention fused); ``--unfused`` runs ``reshape_and_cache`` then
+``paged_attention_decode``.  There is no copy-on-write in this workload
+(``copy_blocks`` has no pairs).
 
 Metric: effective KV read GB/s = (sum_b T_b * Hkv * D * 2 tensors * 2 bytes)
 / step time.  The cache is rotated over enough independent copies (> 1 GiB in
@@ -131,6 +133,8 @@ def main() -> int:
     ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "generic"])
     ap.add_argument("--stream-waves", type=int, default=0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step = reshape_and_cache + paged_attention_decode (two launches)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -189,15 +193,21 @@ def main() -> int:
     workspace = pkv.DecodeWorkspace(device=dev)
     stream = torch.cuda.current_stream()
 
+    kw = dict(max_seq_len=max_len, partition_size=ps, waves_per_group=args.waves,
+              kernel=args.kernel, stream_waves=args.stream_waves, workspace=workspace)
+
     def step(i, ev=None):
         kc, vc = caches[i % copies]
-        pkv.reshape_and_cache(k_new, v_new, slots_new, kc, vc)
-        if ev is not None:
-            ev[0].record(stream)
-        pkv.paged_attention_decode(q, kc, vc, bt, lens, bs, w.scale, out, max_seq_len=max_len,
-                                   partition_size=ps, waves_per_group=args.waves,
-                                   kernel=args.kernel, stream_waves=args.stream_waves,
-                                   workspace=workspace)
+        if args.unfused:
+            pkv.reshape_and_cache(k_new, v_new, slots_new, kc, vc)
+            if ev is not None:
+                ev[0].record(stream)
+            pkv.paged_attention_decode(q, kc, vc, bt, lens, bs, w.scale, out, **kw)
+        else:
+            if ev is not None:
+                ev[0].record(stream)
+            pkv.paged_attention_decode_append(q, k_new, v_new, kc, vc, bt, lens, bs, w.scale, out,
+                                              **kw)
         if ev is not None:
             ev[1].record(stream)
 
@@ -206,25 +216,34 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # The timed region: K steps back to back between one pair of events on the
+    # stream the kernels run on.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
-    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    log(f"step {ms_step * 1e3:.2f} us, decode call {decode_ms * 1e3:.2f} us")
+    if args.unfused:
+        # the decode launch on its own: one event pair around each launch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(args.warmup + args.steps + i, evs[i])
+        torch.cuda.synchronize()
+        decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    else:
+        decode_ms = ms_step  # the step is the one launch
+    log(f"step {ms_step * 1e3:.2f} us, decode launch {decode_ms * 1e3:.2f} us")
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
     kernel_name = {"auto": "stream" if not ps else "mfma"}.get(args.kernel, args.kernel)
-    traffic = measured_traffic(w.name, kernel_name)
+    traffic = measured_traffic(w.name, kernel_name + ("" if args.unfused else "+append"))
     result = {
         "metric": "effective KV read GB/s (% of MI355X HBM peak) in paged decode attention",
         "value": round(value, 2),
@@ -243,13 +262,16 @@ def main() -> int:
             "head_dim": d, "block_size": bs, "total_tokens": w.total_tokens,
             "kv_bytes_per_step": kv_bytes, "cache_copies_rotated": copies,
             "partition_size": ps or "library", "kernel": kernel_name,
+            "step_launches": ("reshape_and_cache + paged_attention_decode" if args.unfused
+                              else "paged_attention_decode_append (write + attention fused)"),
             "hbm_peak_frac_of_step": round(value / HBM_PEAK_GBS, 4),
             "tokens_per_s_per_layer_step": round(s / (ms_step * 1e-3), 1),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": f"paged_attention_decode ({kernel_name} kernel, one launch)",
+            "kernel": (f"paged_attention_decode ({kernel_name} kernel, one launch)" if args.unfused
+                       else f"paged_attention_decode_append ({kernel_name} kernel, one launch)"),
             "algorithmic_bytes_per_launch": kv_bytes,
             "avg_launch_us": round(decode_ms * 1e3, 3),
         },

@@ -176,6 +176,31 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache,
                                       const pkv_decode_dims* dims, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* One decode step in one call: the cache write of each sequence's new token
+ * followed by paged decode attention over its T_b tokens [ITH §手動畫一次
+ * block table: a new token fills the tail block's next slot; PU §按 Block
+ * 分配: position t lives at offset t % B of the block its table gives for
+ * logical block t / B].  Equivalent to pkv_reshape_and_cache with
+ * slot_mapping[b] = bt[b][(T_b - 1) / B] * B + (T_b - 1) % B, followed by
+ * pkv_paged_attention_decode with the same arguments; the stream kernel does
+ * both in one launch (the wavefront that folds a sequence's last chunk writes
+ * the token and uses it), the other kernel families run a small write kernel
+ * first.
+ *   k_new, v_new  bf16 [S, Hkv, D] contiguous, 16-byte aligned; the K and V of
+ *                 position T_b - 1 of every sequence.  Sequences with T_b == 0
+ *                 are left alone (nothing is written; their output row is 0).
+ *   k_cache, v_cache  written (one slot per sequence and KV head) and read.
+ * The block holding position T_b - 1 must belong to sequence b alone (copy a
+ * shared tail with pkv_copy_blocks first).  Other arguments, the workspace
+ * and the return codes as for pkv_paged_attention_decode. */
+pkv_status pkv_paged_attention_decode_append(const void* q, const void* k_new, const void* v_new,
+                                             void* k_cache, void* v_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* seq_lens, int32_t block_size,
+                                             float scale, void* out, const pkv_decode_dims* dims,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream);
+
 /* Slot-mapped cache write [ITH §手動畫一次 block table: the next token goes
  * into the tail block's next free slot; PU §按 Block 分配: new tokens fill the
  * tail block first].  For n in [0, num_tokens) with s = slot_mapping[n] >= 0:

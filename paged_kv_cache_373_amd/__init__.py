@@ -20,7 +20,8 @@ import torch
 from .block_manager import BlockManager, PoolExhaustedError, slot_mapping_for
 
 __all__ = [
-    "lib", "paged_attention_decode", "reshape_and_cache", "copy_blocks",
+    "lib", "paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
+    "copy_blocks",
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
     "BlockManager",
     "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
@@ -78,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.pkv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
         L.pkv_paged_attention_decode.restype = ctypes.c_int
+        L.pkv_paged_attention_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32,
+                                                        ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.pkv_paged_attention_decode_append.restype = ctypes.c_int
         L.pkv_reshape_and_cache.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, vp]
         L.pkv_reshape_and_cache.restype = ctypes.c_int
         L.pkv_copy_blocks.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i64,
@@ -204,19 +208,9 @@ def _default_workspace(device: torch.device) -> DecodeWorkspace:
     return ws
 
 
-def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                           block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
-                           scale: float, out: torch.Tensor, *, max_seq_len: Optional[int] = None,
-                           partition_size: int = 0, kernel: str = "auto",
-                           waves_per_group: int = 0, balance_partitions: bool = False,
-                           stream_waves: int = 0, workspace=None,
-                           stream=None) -> torch.Tensor:
-    """Single-query paged decode attention ([ITH §PagedAttention 的核心想法];
-    [PU §按 Block 分配]).  Writes ``out`` [S, Hq, D] (bf16 or fp32) and returns
-    it.  ``max_seq_len`` defaults to the table capacity (max_blocks * B).
-    ``workspace`` is a :class:`DecodeWorkspace` (reused across calls; the
-    default is one per device) or a raw uint8 device tensor, whose counter
-    region is then cleared before every call."""
+def _decode(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale, out,
+            max_seq_len, partition_size, kernel, waves_per_group, balance_partitions,
+            stream_waves, workspace, stream) -> torch.Tensor:
     _check(q, "q", torch.bfloat16, 3)
     _check(k_cache, "k_cache", torch.bfloat16, 4)
     _check(v_cache, "v_cache", torch.bfloat16, 4)
@@ -231,6 +225,11 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
         raise ValueError("cache shapes must be k [P,Hkv,B,D] and v [P,Hkv,D,B] matching q")
     if tuple(out.shape) != (s, hq, d) or block_tables.shape[0] != s or seq_lens.shape[0] != s:
         raise ValueError("q, out, block_tables and seq_lens disagree on the batch")
+    if k_new is not None:
+        _check(k_new, "k_new", torch.bfloat16, 3)
+        _check(v_new, "v_new", torch.bfloat16, 3)
+        if tuple(k_new.shape) != (s, hkv, d) or tuple(v_new.shape) != (s, hkv, d):
+            raise ValueError("k_new and v_new must be [S, Hkv, D]")
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out.dtype, kernel,
                  waves_per_group, balance_partitions, stream_waves)
     L = lib()
@@ -253,13 +252,56 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
             if zeroed:
                 _zero_prefix(buf, zeroed, stream)
         ws_ptr, ws_len = buf.data_ptr(), buf.numel()
-    st = L.pkv_paged_attention_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                      block_tables.data_ptr(), seq_lens.data_ptr(), bs,
-                                      float(scale), out.data_ptr(), ctypes.byref(dims), ws_ptr,
-                                      ws_len, _stream(stream))
+    if k_new is None:
+        st = L.pkv_paged_attention_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                          block_tables.data_ptr(), seq_lens.data_ptr(), bs,
+                                          float(scale), out.data_ptr(), ctypes.byref(dims),
+                                          ws_ptr, ws_len, _stream(stream))
+        what = "pkv_paged_attention_decode"
+    else:
+        st = L.pkv_paged_attention_decode_append(
+            q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+            v_cache.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(), bs, float(scale),
+            out.data_ptr(), ctypes.byref(dims), ws_ptr, ws_len, _stream(stream))
+        what = "pkv_paged_attention_decode_append"
     if st != PKV_OK:
-        raise PagedKVError(st, "pkv_paged_attention_decode")
+        raise PagedKVError(st, what)
     return out
+
+
+def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                           scale: float, out: torch.Tensor, *, max_seq_len: Optional[int] = None,
+                           partition_size: int = 0, kernel: str = "auto",
+                           waves_per_group: int = 0, balance_partitions: bool = False,
+                           stream_waves: int = 0, workspace=None,
+                           stream=None) -> torch.Tensor:
+    """Single-query paged decode attention ([ITH §PagedAttention 的核心想法];
+    [PU §按 Block 分配]).  Writes ``out`` [S, Hq, D] (bf16 or fp32) and returns
+    it.  ``max_seq_len`` defaults to the table capacity (max_blocks * B).
+    ``workspace`` is a :class:`DecodeWorkspace` (reused across calls; the
+    default is one per device) or a raw uint8 device tensor, whose counter
+    region is then cleared before every call."""
+    return _decode(q, None, None, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
+                   out, max_seq_len, partition_size, kernel, waves_per_group,
+                   balance_partitions, stream_waves, workspace, stream)
+
+
+def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                  block_size: int, scale: float, out: torch.Tensor, *,
+                                  max_seq_len: Optional[int] = None, partition_size: int = 0,
+                                  kernel: str = "auto", waves_per_group: int = 0,
+                                  balance_partitions: bool = False, stream_waves: int = 0,
+                                  workspace=None, stream=None) -> torch.Tensor:
+    """One decode step: writes k_new/v_new [S, Hkv, D] (the token at position
+    T_b - 1 of each sequence) into the slot its block table gives, then
+    attends over the T_b tokens ([ITH §手動畫一次 block table]; [PU §按 Block
+    分配]).  With the stream kernel both happen in one launch."""
+    return _decode(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
+                   out, max_seq_len, partition_size, kernel, waves_per_group,
+                   balance_partitions, stream_waves, workspace, stream)
 
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,

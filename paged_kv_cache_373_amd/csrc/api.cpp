@@ -37,10 +37,11 @@ int32_t default_partition(const pkv_decode_dims* d, int32_t block_size) {
 
 enum Family { kGeneric, kMfma, kStream };
 
-// Wavefronts the stream kernel launches by default: 8 per compute unit of an
-// MI355X (256 CUs), enough bytes in flight to saturate HBM with every
-// wavefront resident from the start; fewer when the problem is small.
-constexpr int32_t kStreamWaveTarget = 2048;
+// Wavefronts the stream kernel launches by default: every one resident from
+// the start on an MI355X (256 CUs) - 8 per CU at head_dim 64 (2 per SIMD), 4
+// per CU at head_dim 128, whose larger operands allow 1 per SIMD - which keeps
+// enough bytes in flight to saturate HBM; fewer when the problem is small.
+int32_t stream_wave_target(int32_t head_dim) { return head_dim <= 64 ? 2048 : 1024; }
 constexpr int32_t kMinChunksPerWave = 4;
 
 struct Plan {
@@ -118,7 +119,7 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
     int64_t wv = d->stream_waves;
     if (wv == 0) {
       wv = (chunk_bound + kMinChunksPerWave - 1) / kMinChunksPerWave;
-      wv = wv < kStreamWaveTarget ? wv : kStreamWaveTarget;
+      wv = wv < stream_wave_target(d->head_dim) ? wv : stream_wave_target(d->head_dim);
       wv = (wv + 3) / 4 * 4;
       if (wv < 4) wv = 4;
     }
@@ -187,16 +188,25 @@ size_t pkv_decode_workspace_zeroed_bytes(const pkv_decode_dims* dims, int32_t bl
   return p.counter_bytes;
 }
 
-pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
-                                      const int32_t* block_tables, const int32_t* seq_lens,
-                                      int32_t block_size, float scale, void* out,
-                                      const pkv_decode_dims* dims, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the decode entry points; k_new / v_new are null for a plain decode.
+pkv_status decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                       int32_t block_size, float scale, void* out, const pkv_decode_dims* dims,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   const Plan p = plan_decode(dims, block_size);
   if (!p.ok) return p.status;
   if (dims->num_seqs == 0) return PKV_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
       seq_lens == nullptr || out == nullptr)
+    return PKV_ERR_INVALID;
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (append && (k_new == nullptr || v_new == nullptr || dims->head_dim % 8 != 0 ||
+                 !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+                 !aligned16(v_cache)))
     return PKV_ERR_INVALID;
   if (!std::isfinite(scale)) return PKV_ERR_INVALID;
   if (p.family != kGeneric && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)))
@@ -233,11 +243,56 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
     a.prm.part_ml = reinterpret_cast<float*>(ws + p.part_ml_offset);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* kc_w = static_cast<uint16_t*>(const_cast<void*>(k_cache));
+  uint16_t* vc_w = static_cast<uint16_t*>(const_cast<void*>(v_cache));
+  if (append && p.family == kStream) {
+    // one launch: the wavefront that folds a unit's last chunk writes the new
+    // token and uses it in place of the slot's old contents
+    a.prm.k_new = static_cast<const uint16_t*>(k_new);
+    a.prm.v_new = static_cast<const uint16_t*>(v_new);
+    a.prm.k_cache_w = kc_w;
+    a.prm.v_cache_w = vc_w;
+  } else if (append) {
+    const hipError_t e = pkv::launch_append_tokens(
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), block_tables,
+        seq_lens, dims->num_seqs, dims->max_blocks_per_seq, dims->num_kv_heads, dims->head_dim,
+        kc_w, vc_w, block_size, s);
+    if (e != hipSuccess) return PKV_ERR_HIP;
+  }
   switch (p.family) {
     case kStream: return hip_status(pkv::launch_decode_stream(a, p.stream_waves, s));
     case kMfma: return hip_status(pkv::launch_decode_mfma(a, p.waves, s));
     default: return hip_status(pkv::launch_decode_generic(a, s));
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_tables, const int32_t* seq_lens,
+                                      int32_t block_size, float scale, void* out,
+                                      const pkv_decode_dims* dims, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, seq_lens, block_size,
+                     scale, out, dims, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attention_decode_append(const void* q, const void* k_new, const void* v_new,
+                                             void* k_cache, void* v_cache,
+                                             const int32_t* block_tables,
+                                             const int32_t* seq_lens, int32_t block_size,
+                                             float scale, void* out, const pkv_decode_dims* dims,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  if (k_new == nullptr || v_new == nullptr) {
+    const Plan p = plan_decode(dims, block_size);
+    if (!p.ok) return p.status;
+    return dims->num_seqs == 0 ? PKV_OK : PKV_ERR_INVALID;
+  }
+  return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
+                     out, dims, workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_reshape_and_cache(const void* k, const void* v, const int64_t* slot_mapping,

@@ -6,6 +6,9 @@
 //                      the next free slot of the tail block; Fanyi Pu,
 //                      "Infra: PagedAttention", section "按 Block 分配": the
 //                      slot is physical block t/B's offset t%B).
+//   append_tokens      the same write for a decode step's one new token per
+//                      sequence, at position T_b - 1 of its block table (the
+//                      non-fused half of pkv_paged_attention_decode_append).
 //   copy_blocks        copies whole blocks src -> dst in every layer (Fanyi Pu,
 //                      "Infra: PagedAttention", section "共享前缀，分叉时
 //                      Copy-on-write": a shared tail block is duplicated before
@@ -55,6 +58,41 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// One thread per 8 features of one (sequence, KV head): the new token of
+// sequence b sits at position T_b - 1, in block table[b][(T_b - 1) / B] at
+// offset (T_b - 1) % B.
+__global__ void __launch_bounds__(256)
+    append_tokens_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                         const int32_t* __restrict__ block_tables,
+                         const int32_t* __restrict__ seq_lens, int64_t num_items,
+                         int32_t max_blocks_per_seq, int32_t num_kv_heads, int32_t head_dim,
+                         uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+                         int32_t block_size) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (item >= num_items) return;
+  const int32_t chunks = head_dim / 8;
+  const int64_t row = item / chunks;  // (sequence, head)
+  const int32_t c8 = static_cast<int32_t>(item - row * chunks);
+  const int64_t b = row / num_kv_heads;
+  const int32_t h = static_cast<int32_t>(row - b * num_kv_heads);
+  const int32_t T = seq_lens[b];
+  if (T <= 0) return;
+  const int32_t t = T - 1;
+  const int64_t blk = block_tables[b * max_blocks_per_seq + t / block_size];
+  const int32_t off = t % block_size;
+  const size_t src = static_cast<size_t>(row) * head_dim + 8 * c8;
+  const size_t tile = (static_cast<size_t>(blk) * num_kv_heads + h) * block_size * head_dim;
+  *reinterpret_cast<u32x4_t*>(k_cache + tile + static_cast<size_t>(off) * head_dim + 8 * c8) =
+      *reinterpret_cast<const u32x4_t*>(k_new + src);
+  const u32x4_t vv = *reinterpret_cast<const u32x4_t*>(v_new + src);
+  uint16_t* vdst = v_cache + tile + static_cast<size_t>(8 * c8) * block_size + off;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vdst[static_cast<size_t>(2 * e) * block_size] = static_cast<uint16_t>(vv[e] & 0xFFFFu);
+    vdst[static_cast<size_t>(2 * e + 1) * block_size] = static_cast<uint16_t>(vv[e] >> 16);
+  }
+}
+
 struct LayerPtrs {
   u32x4_t* k[kMaxCopyLayers];
   u32x4_t* v[kMaxCopyLayers];
@@ -85,6 +123,20 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v,
   const int64_t blocks = (items + 255) / 256;
   reshape_and_cache_kernel<<<dim3(static_cast<uint32_t>(blocks)), 256, 0, stream>>>(
       k, v, slot_mapping, items, num_kv_heads, head_dim, k_cache, v_cache, block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_tokens(const uint16_t* k_new, const uint16_t* v_new,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_kv_heads,
+                                int32_t head_dim, uint16_t* k_cache, uint16_t* v_cache,
+                                int32_t block_size, hipStream_t stream) {
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * (head_dim / 8);
+  if (items == 0) return hipSuccess;
+  const int64_t blocks = (items + 255) / 256;
+  append_tokens_kernel<<<dim3(static_cast<uint32_t>(blocks)), 256, 0, stream>>>(
+      k_new, v_new, block_tables, seq_lens, items, max_blocks_per_seq, num_kv_heads, head_dim,
+      k_cache, v_cache, block_size);
   return hipGetLastError();
 }
 

@@ -314,8 +314,8 @@ constexpr int kStreamWaves = 4;       // wavefronts per workgroup, each with its
 constexpr int kStreamMaxSeqs = 2048;  // sequences whose lengths and prefix fit in LDS
 
 template <int D, int BS>
-__global__ void __launch_bounds__(kStreamWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
-    decode_stream(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+__global__ void __launch_bounds__(kStreamWaves * 64)
+    __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) decode_stream(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                   const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
                   const int32_t* __restrict__ seq_lens, const DecodeParams prm) {
   using M = Mfma<D, BS>;
@@ -565,7 +565,8 @@ __global__ void __launch_bounds__(kStreamWaves * 64) __attribute__((amdgpu_waves
       chd = rem / nb;
       clc = rem - chd * nb;
       cval = min(32, T - 32 * clc);
-      cfl = ((cc == start || clc == 0) ? 1 : 0) | ((cc == end - 1 || clc == nb - 1) ? 2 : 0);
+      cfl = ((cc == start || clc == 0) ? 1 : 0) | ((cc == end - 1 || clc == nb - 1) ? 2 : 0) |
+            (clc == nb - 1 ? 4 : 0);
       const int last_blk = (T + BS - 1) / BS - 1;
       const int32_t* row = block_tables + static_cast<size_t>(lo) * MB;
 #pragma unroll
@@ -592,7 +593,64 @@ __global__ void __launch_bounds__(kStreamWaves * 64) __attribute__((amdgpu_waves
         // the join then stay those of the chunk ring
         __builtin_amdgcn_s_waitcnt(0);
       }
-      M::step(qop, x, __builtin_amdgcn_readlane(cval, i), sl, c, st);
+      const int valid = __builtin_amdgcn_readlane(cval, i);
+      if ((fl & 4) && prm.k_new != nullptr) {
+        // The unit's last chunk holds the new token (chunk position
+        // valid - 1): its K/V come from k_new/v_new into the operand registers
+        // (the cache slot was read before it is written), then go to the slot.
+        const int tn = valid - 1;
+        const int hh = __builtin_amdgcn_readlane(chd, i);
+        const size_t src = (static_cast<size_t>(__builtin_amdgcn_readlane(cb, i)) * Hkv + hh) * D;
+        const int un = (tn & 7) >> 2;            // K operand half holding the token
+        const int rn = 4 * (tn >> 3) + (tn & 3); // and its lane row
+        const int cn = tn >> 3;                  // V operand lane group holding the token
+        const int en = tn & 7;                   // and its element
+        bf16x8_t kn[HS];
+#pragma unroll
+        for (int hs = 0; hs < HS; ++hs) kn[hs] = load_bf16x8(prm.k_new + src + 32 * hs + 8 * c);
+        uint16_t vn[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) vn[nt] = prm.v_new[src + 16 * nt + r];
+        __builtin_amdgcn_s_waitcnt(0);
+        const bool in0 = (r == rn) && (un == 0);
+        const bool in1 = (r == rn) && (un == 1);
+#pragma unroll
+        for (int hs = 0; hs < HS; ++hs) {
+          const u32x4_t nk = __builtin_bit_cast(u32x4_t, kn[hs]);
+          const u32x4_t o0 = __builtin_bit_cast(u32x4_t, x.k[0][hs]);
+          const u32x4_t o1 = __builtin_bit_cast(u32x4_t, x.k[1][hs]);
+          u32x4_t r0, r1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r0[e] = in0 ? nk[e] : o0[e];
+            r1[e] = in1 ? nk[e] : o1[e];
+          }
+          x.k[0][hs] = __builtin_bit_cast(bf16x8_t, r0);
+          x.k[1][hs] = __builtin_bit_cast(bf16x8_t, r1);
+        }
+        if (c == cn) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              x.v[nt][e] = (e == en) ? __builtin_bit_cast(__bf16, vn[nt]) : x.v[nt][e];
+        }
+        // slot of the new token: block tn / BS of the chunk, offset tn % BS
+        int blk = __builtin_amdgcn_readlane(ent[0], i);
+#pragma unroll
+        for (int j = 1; j < NB; ++j)
+          blk = (tn / BS == j) ? __builtin_amdgcn_readlane(ent[j], i) : blk;
+        const size_t tile = (static_cast<size_t>(blk) * Hkv + hh) * M::kTile;
+        const int off = tn % BS;
+        if (lane < 4 * HS) {  // K row: HS x 4 pieces of 16 bytes
+          const int hs = lane >> 2, cc4 = lane & 3;
+          *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 32 * hs + 8 * cc4) =
+              *reinterpret_cast<const u32x4_t*>(prm.k_new + src + 32 * hs + 8 * cc4);
+        }
+        for (int d = lane; d < D; d += 64) prm.v_cache_w[tile + static_cast<size_t>(d) * BS + off] =
+            prm.v_new[src + d];
+      }
+      M::step(qop, x, valid, sl, c, st);
       if (fl & 2) finish_piece(__builtin_amdgcn_readlane(clc, i));
     };
 

@@ -32,6 +32,12 @@ struct DecodeParams {
                               // (matrix-core kernel; shares memory with part_lse)
   uint32_t* counters;         // [S, Hkv] finished partitions per (sequence, KV head);
                               // zero before and after every call
+  // Decode step with append (stream kernel): each sequence's new token, at
+  // position T_b - 1, is written to the slot its table gives and attended.
+  const uint16_t* k_new;      // bf16 [S, Hkv, D], or null
+  const uint16_t* v_new;      // bf16 [S, Hkv, D]
+  uint16_t* k_cache_w;        // the caches, for the new tokens' writes
+  uint16_t* v_cache_w;
 };
 
 struct DecodeLaunch {
@@ -63,6 +69,14 @@ hipError_t launch_merge(const float* part_out, const float* part_lse, int32_t nu
                         int32_t part_stride, int32_t num_parts, int32_t head_dim,
                         const int32_t* seq_lens, int32_t rows_per_seq,
                         int32_t partition_size, void* out, int out_f32, hipStream_t stream);
+
+// Writes k_new/v_new of sequence b (T_b >= 1) to the slot of position T_b - 1
+// given by its block table; sequences with T_b == 0 are skipped.
+hipError_t launch_append_tokens(const uint16_t* k_new, const uint16_t* v_new,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_kv_heads,
+                                int32_t head_dim, uint16_t* k_cache, uint16_t* v_cache,
+                                int32_t block_size, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v,
                                     const int64_t* slot_mapping, int32_t num_tokens,

@@ -142,6 +142,21 @@ def test_decode_rejects_before_any_hip_call():
     assert call(dims=ctypes.byref(empty)) == pkv.PKV_OK  # nothing to do
 
 
+def test_append_rejects_before_any_hip_call():
+    lib = pkv.lib()
+    dims = _dims()
+    f = ctypes.c_void_p(0x1000)
+    call = lambda kn, vn, d=dims: lib.pkv_paged_attention_decode_append(
+        f, kn, vn, f, f, f, f, 16, 0.125, f, ctypes.byref(d), f, 1 << 20, None)
+    lib.pkv_paged_attention_decode_append.argtypes = [ctypes.c_void_p] * 7 + [
+        ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(pkv.DecodeDims),
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert call(None, f) == pkv.PKV_ERR_INVALID
+    assert call(f, None) == pkv.PKV_ERR_INVALID
+    assert call(ctypes.c_void_p(0x1008), f) == pkv.PKV_ERR_INVALID  # misaligned k_new
+    assert call(f, f, _dims(num_q_heads=30)) == pkv.PKV_ERR_INVALID
+
+
 def test_writers_reject_before_any_hip_call():
     lib = pkv.lib()
     f = ctypes.c_void_p(0x1000)
