@@ -244,6 +244,21 @@ def pool_layer_q(layer: int, num_seqs: int = 256, wid: int = 5) -> np.ndarray:
     return normal_bf16(rng(wid, _ROLE_Q, layer), (num_seqs, 32, 64))
 
 
+def pool_layer_tokens_device(layer: int, num_tokens: int, device, block_size: int,
+                             wid: int = 5):
+    """K and V (bf16 [num_tokens, 8, 64]) of every token of one layer of the
+    pool workload, drawn on the device: the full step holds ~15 GB of KV,
+    too much to draw on the host.  torch's seeded device generator, N(0, 1)
+    rounded to bf16; sampled rows are copied back for the oracle."""
+    import torch
+
+    seed = int(np.random.SeedSequence([SEED, wid, _ROLE_K, layer, block_size]).generate_state(1)[0])
+    g = torch.Generator(device=device).manual_seed(seed)
+    k = torch.randn((num_tokens, 8, 64), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((num_tokens, 8, 64), generator=g, device=device, dtype=torch.float32)
+    return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
 def pool_layer_tokens(layer: int, seq: int, length: int, wid: int = 5):
     """K and V (bf16 bits, [length, 8, 64]) of one sequence in one layer."""
     k = normal_bf16(rng(wid, _ROLE_K, layer, seq), (length, 8, 64))
