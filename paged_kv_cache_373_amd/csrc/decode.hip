@@ -393,27 +393,23 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
   const size_t blk_stride = static_cast<size_t>(Hkv) * M::kTile;
   typename M::State st;
   st.reset();
-  bf16x8_t qop[HS];
+  struct Slot {  // one ring entry: a chunk's K/V operands and its unit's query group
+    Regs x;
+    bf16x8_t q[HS];
+  };
   int pb = 0, ph = 0, plc0 = 0;  // the piece being folded: sequence, KV head, first chunk
 
-  // Ends the current piece whose last chunk is `last_lc` of its unit.
-  auto finish_piece = [&](int last_lc) {
-    const int T = s_len[pb];
-    const int nb = (T + 31) >> 5;
-    const size_t row0 = static_cast<size_t>(pb) * Hq + static_cast<size_t>(ph) * G;
-    if (plc0 == 0 && last_lc == nb - 1) {  // the whole unit: final output
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gh = 4 * c + i;
-        if (gh < G) {
-          const float inv = 1.0f / st.lsum[i];
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            store_out(prm.out, (row0 + gh) * D + 16 * nt + r, st.acc[nt][i] * inv, prm.out_f32);
-        }
-      }
-      return;
-    }
+  // The pieces of unit (sb, sh): one per wavefront from the owner of the
+  // unit's first chunk (gf) to the owner of its last (gl).
+  auto unit_span = [&](int sb, int sh, int64_t& gf, int64_t& gl) {
+    const int nb = (s_len[sb] + 31) >> 5;
+    const int64_t cu0 = static_cast<int64_t>(Hkv) * s_pre[sb] + static_cast<int64_t>(sh) * nb;
+    gf = ((cu0 + 1) * Weff - 1) / C;
+    gl = ((cu0 + nb) * Weff - 1) / C;
+  };
+  // Publishes the state of the current piece (a part of unit (pb, ph)) into
+  // workspace slot u + g with device-coherent stores.
+  auto publish = [&]() {
     const int64_t u = static_cast<int64_t>(pb) * Hkv + ph;
     float* pacc = prm.part_out + (u + g) * G * D;  // [G][D]
     float* pml = prm.part_ml + (u + g) * G * 2;    // [G][max, sum]
@@ -427,19 +423,25 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       }
     }
     if (c == 0 && r < G) store_coherent(pml + r * 2, st.m2);
-    // the stores are complete (visible chip-wide) before the count is made
-    __builtin_amdgcn_s_waitcnt(0);
+  };
+  // Counts a published piece of unit (sb, sh) whose stores have completed;
+  // returns the count before this arrival.
+  auto count = [&](int sb, int sh) -> uint32_t {
     uint32_t prev = 0;
     if (lane == 0)
-      prev = __hip_atomic_fetch_add(prm.counters + u, 1u, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    const int64_t cu0 = static_cast<int64_t>(Hkv) * s_pre[pb] + static_cast<int64_t>(ph) * nb;
-    const int64_t gf = ((cu0 + 1) * Weff - 1) / C;   // owner of the unit's first chunk
-    const int64_t gl = ((cu0 + nb) * Weff - 1) / C;  // owner of its last chunk
-    if (prev != static_cast<uint32_t>(gl - gf)) return;
-    // Last piece: merge the unit's k pieces in wavefront order (so the result
-    // does not depend on which piece arrived last).  Their (max, sum) pairs
+      prev = __hip_atomic_fetch_add(prm.counters + static_cast<int64_t>(sb) * Hkv + sh, 1u,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return prev;
+  };
+  // Merges every piece of unit (sb, sh) - all published and counted - into
+  // the output, in wavefront order, and leaves its counter at zero.
+  auto merge_unit = [&](int sb, int sh) {
+    const int64_t u = static_cast<int64_t>(sb) * Hkv + sh;
+    const size_t row0 = static_cast<size_t>(sb) * Hq + static_cast<size_t>(sh) * G;
+    int64_t gf, gl;
+    unit_span(sb, sh, gf, gl);
+    // Merge the unit's k pieces in wavefront order (so the result does not
+    // depend on which piece arrived last).  Their (max, sum) pairs
     // go to this wavefront's LDS area, all loads in flight at once; then each
     // lane folds four adjacent features of one head, sixteen pieces' loads at
     // a time.
@@ -539,6 +541,40 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
     if (lane == 0)
       __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
+  // A wavefront's range is contiguous, so only its first and its last piece
+  // can be parts of units; every unit in between is whole.  Partial pieces
+  // are published when they end and counted together once the range is done
+  // - one wait for all stores, then both counts - so the chunk ring never
+  // drains in mid-range.
+  int np_pub = 0, pub_b0 = 0, pub_h0 = 0, pub_b1 = 0, pub_h1 = 0;
+  // Ends the current piece whose last chunk is `last_lc` of its unit.
+  auto finish_piece = [&](int last_lc) {
+    const int T = s_len[pb];
+    const int nb = (T + 31) >> 5;
+    const size_t row0 = static_cast<size_t>(pb) * Hq + static_cast<size_t>(ph) * G;
+    if (plc0 == 0 && last_lc == nb - 1) {  // the whole unit: final output
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gh = 4 * c + i;
+        if (gh < G) {
+          const float inv = 1.0f / st.lsum[i];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            store_out(prm.out, (row0 + gh) * D + 16 * nt + r, st.acc[nt][i] * inv, prm.out_f32);
+        }
+      }
+      return;
+    }
+    publish();
+    if (np_pub == 0) {
+      pub_b0 = pb;
+      pub_h0 = ph;
+    } else {
+      pub_b1 = pb;
+      pub_h1 = ph;
+    }
+    ++np_pub;
+  };
 
   for (int64_t bat = start; bat < end; bat += 64) {
     const int n = static_cast<int>(end - bat < 64 ? end - bat : 64);
@@ -573,25 +609,26 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       for (int j = 0; j < NB; ++j) ent[j] = row[min(clc * kBlocksPerChunk + j, last_blk)];
     }
 
-    auto issue = [&](int i, Regs& x) {
-      const size_t head_off = static_cast<size_t>(__builtin_amdgcn_readlane(chd, i)) * M::kTile;
+    auto issue = [&](int i, Slot& sl8) {
+      const int hh = __builtin_amdgcn_readlane(chd, i);
+      const size_t head_off = static_cast<size_t>(hh) * M::kTile;
       size_t base[NB];
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         base[j] = static_cast<size_t>(__builtin_amdgcn_readlane(ent[j], i)) * blk_stride + head_off;
-      M::load(k_cache, v_cache, base, ln, x);
+      M::load(k_cache, v_cache, base, ln, sl8.x);
+      // the chunk's query group travels with it (512 bytes per unit, cached
+      // after its first chunk), so a piece starting needs no load of its own
+      M::load_q(q, Hq, G, __builtin_amdgcn_readlane(cb, i), hh, c, r, sl8.q);
     };
-    auto consume = [&](int i, Regs& x) {
+    auto consume = [&](int i, Slot& sl8) {
+      Regs& x = sl8.x;
       const int fl = __builtin_amdgcn_readlane(cfl, i);
-      if (fl & 1) {  // a piece starts: its query group, a fresh state
+      if (fl & 1) {  // a piece starts: a fresh state
         pb = __builtin_amdgcn_readlane(cb, i);
         ph = __builtin_amdgcn_readlane(chd, i);
         plc0 = __builtin_amdgcn_readlane(clc, i);
         st.reset();
-        M::load_q(q, Hq, G, pb, ph, c, r, qop);
-        // wait for the query here, inside the branch: the wait counts after
-        // the join then stay those of the chunk ring
-        __builtin_amdgcn_s_waitcnt(0);
       }
       const int valid = __builtin_amdgcn_readlane(cval, i);
       if ((fl & 4) && prm.k_new != nullptr) {
@@ -650,13 +687,13 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
         for (int d = lane; d < D; d += 64) prm.v_cache_w[tile + static_cast<size_t>(d) * BS + off] =
             prm.v_new[src + d];
       }
-      M::step(qop, x, valid, sl, c, st);
+      M::step(sl8.q, x, valid, sl, c, st);
       if (fl & 2) finish_piece(__builtin_amdgcn_readlane(clc, i));
     };
 
     // Ring of DEPTH chunks in flight; the steady-state refills are
     // unconditional so the wait counts stay exact, only the drain is not.
-    Regs ring[DEPTH];
+    Slot ring[DEPTH];
     if (n >= DEPTH) {
 #pragma unroll
       for (int s = 0; s < DEPTH; ++s) issue(s, ring[s]);
@@ -683,6 +720,22 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
 #pragma unroll
       for (int s = 0; s < DEPTH; ++s)
         if (s < n) consume(s, ring[s]);
+    }
+  }
+
+  // Count the published pieces (their stores complete first) and merge each
+  // unit this wavefront closed.
+  if (np_pub > 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint32_t prev0 = count(pub_b0, pub_h0);
+    const uint32_t prev1 = np_pub > 1 ? count(pub_b1, pub_h1) : 0u;
+    for (int t = 0; t < np_pub; ++t) {
+      const int sb = t == 0 ? pub_b0 : pub_b1;
+      const int sh = t == 0 ? pub_h0 : pub_h1;
+      int64_t gf, gl;
+      unit_span(sb, sh, gf, gl);
+      const uint32_t prev = __builtin_amdgcn_readfirstlane(t == 0 ? prev0 : prev1);
+      if (prev == static_cast<uint32_t>(gl - gf)) merge_unit(sb, sh);
     }
   }
 }
