@@ -42,7 +42,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 ROTATE_BYTES = 1 << 30
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_373_amd", "csrc", "decode.hip")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_373_amd", "csrc", f)
+                  for f in ("chunk.h", "decode.hip", "decode_wg.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
@@ -67,8 +68,12 @@ def make_workload(name: str):
 
 
 def source_digest() -> str:
-    with open(DECODE_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the decode kernels' sources, in a fixed order."""
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -130,7 +135,8 @@ def main() -> int:
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: >1 GiB)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "stream", "mfma", "generic"])
+    ap.add_argument("--kernel", default="auto",
+                    choices=["auto", "stream_wg", "stream", "mfma", "generic"])
     ap.add_argument("--stream-waves", type=int, default=0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     ap.add_argument("--unfused", action="store_true",
@@ -242,7 +248,8 @@ def main() -> int:
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
-    kernel_name = {"auto": "stream" if not ps else "mfma"}.get(args.kernel, args.kernel)
+    kernel_name = pkv.decode_plan_kernel(q, caches[0][0], bt, **{
+        k: v for k, v in kw.items() if k not in ("workspace",)})
     traffic = measured_traffic(w.name, kernel_name + ("" if args.unfused else "+append"))
     result = {
         "metric": "effective KV read GB/s (% of MI355X HBM peak) in paged decode attention",

@@ -76,18 +76,27 @@ typedef enum { PKV_DTYPE_BF16 = 0, PKV_DTYPE_F32 = 1 } pkv_dtype;
  *            32-token chunk) work out evenly to a fixed set of wavefronts;
  *            head_dim 64 or 128, block_size 8/16/32, group <= 16,
  *            num_seqs <= 2048.  Ignores partition_size.
+ *   STREAM_WG  the same work dealt out in equal windows to whole workgroups
+ *            (one per compute unit, 8 wavefronts at head_dim 64, 4 at 128)
+ *            whose wavefronts take the window's chunks one at a time, so they
+ *            finish together; same shape limits.  A window holds as many
+ *            chunks as the workgroup's LDS has slots for; when the chunk bound
+ *            (from max_seq_len) needs more, each workgroup walks several
+ *            windows.  Results do not depend on the timing of the wavefronts.
  *   MFMA     matrix-core kernel over split-KV partitions of partition_size
  *            tokens (a multiple of 32, at most 128 blocks); same head_dim,
  *            block_size and group limits.
  *   GENERIC  vector kernel: any head_dim <= 256, block_size >= 1, group.
- * AUTO picks STREAM when partition_size is 0 and the shape allows it, then
- * MFMA, then GENERIC.  An explicit family whose limits the shape exceeds
+ * AUTO picks STREAM_WG when partition_size is 0, the shape allows it and
+ * one window per workgroup holds the chunk bound, else STREAM when
+ * partition_size is 0 and the shape allows it, then MFMA, then GENERIC.  An explicit family whose limits the shape exceeds
  * gives PKV_ERR_UNSUPPORTED. */
 typedef enum {
   PKV_KERNEL_AUTO = 0,
   PKV_KERNEL_MFMA = 1,
   PKV_KERNEL_GENERIC = 2,
-  PKV_KERNEL_STREAM = 3
+  PKV_KERNEL_STREAM = 3,
+  PKV_KERNEL_STREAM_WG = 4
 } pkv_kernel;
 
 /* Problem description for pkv_paged_attention_decode. */
@@ -113,9 +122,10 @@ typedef struct {
                                  ceil(T / partition_size) partitions that share
                                  its 32-token chunks evenly.  A library-chosen
                                  partition_size always balances.                     */
-  int32_t stream_waves;       /* stream kernel: wavefronts launched, a multiple of 4
-                                 (each takes an equal share of the work);
-                                 0 = library choice                                  */
+  int32_t stream_waves;       /* stream kernels: wavefronts launched, a multiple of 4
+                                 (STREAM: each takes an equal share of the work;
+                                 STREAM_WG: rounded up to whole workgroups, each
+                                 taking an equal share); 0 = library choice          */
 } pkv_decode_dims;
 
 /* Bytes of scratch that pkv_paged_attention_decode needs for `dims` and
@@ -138,6 +148,12 @@ size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size
  * pkv_paged_attention_decode starts (and are zero again when it completes);
  * (size_t)-1 when the arguments are invalid. */
 size_t pkv_decode_workspace_zeroed_bytes(const pkv_decode_dims* dims, int32_t block_size);
+
+/* The kernel family pkv_paged_attention_decode runs for `dims` and
+ * `block_size`: a pkv_kernel value other than PKV_KERNEL_AUTO (the family
+ * AUTO resolves to, or the explicit one), or -1 when the arguments are invalid
+ * or the requested family does not support the shape.  Touches no device. */
+int32_t pkv_decode_plan_kernel(const pkv_decode_dims* dims, int32_t block_size);
 
 /* Single-query paged decode attention with GQA [ITH §PagedAttention 的核心想法:
  * the attention formula is unchanged, the kernel looks the block table up and

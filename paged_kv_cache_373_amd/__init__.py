@@ -31,7 +31,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = 0, -1, -2, -3, -4
 _DTYPES = {torch.bfloat16: 0, torch.float32: 1}
-_KERNELS = {"auto": 0, "mfma": 1, "generic": 2, "stream": 3}
+_KERNELS = {"auto": 0, "mfma": 1, "generic": 2, "stream": 3, "stream_wg": 4}
 
 
 class PagedKVError(RuntimeError):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_decode_workspace_size.restype = sz
         L.pkv_decode_workspace_zeroed_bytes.argtypes = [dims_p, i32]
         L.pkv_decode_workspace_zeroed_bytes.restype = sz
+        L.pkv_decode_plan_kernel.argtypes = [dims_p, i32]
+        L.pkv_decode_plan_kernel.restype = i32
         L.pkv_paged_attention_decode.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_float, vp,
                                                  dims_p, vp, sz, vp]
         L.pkv_paged_attention_decode.restype = ctypes.c_int
@@ -147,6 +149,20 @@ def decode_workspace_size(q, k_cache, block_tables, *, max_seq_len=None, partiti
     if n == ctypes.c_size_t(-1).value:
         raise PagedKVError(PKV_ERR_INVALID, "pkv_decode_workspace_size")
     return int(n)
+
+
+def decode_plan_kernel(q, k_cache, block_tables, *, max_seq_len=None, partition_size=0,
+                       out_dtype=torch.bfloat16, kernel="auto", waves_per_group=0,
+                       balance_partitions=False, stream_waves=0) -> str:
+    """Name of the kernel family a decode call with these arguments runs
+    (what ``kernel="auto"`` resolves to)."""
+    dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
+                 waves_per_group, balance_partitions, stream_waves)
+    k = lib().pkv_decode_plan_kernel(ctypes.byref(dims), k_cache.shape[2])
+    names = {v: n for n, v in _KERNELS.items()}
+    if k not in names or k == 0:
+        raise PagedKVError(PKV_ERR_INVALID, "pkv_decode_plan_kernel")
+    return names[k]
 
 
 def _zero_prefix(buf: torch.Tensor, n: int, stream) -> None:

@@ -35,7 +35,7 @@ int32_t default_partition(const pkv_decode_dims* d, int32_t block_size) {
   return ps;
 }
 
-enum Family { kGeneric, kMfma, kStream };
+enum Family { kGeneric, kMfma, kStream, kStreamWg };
 
 // Wavefronts the stream kernel launches by default: every one resident from
 // the start on an MI355X (256 CUs) - 8 per CU at head_dim 64 (2 per SIMD), 4
@@ -43,6 +43,10 @@ enum Family { kGeneric, kMfma, kStream };
 // enough bytes in flight to saturate HBM; fewer when the problem is small.
 int32_t stream_wave_target(int32_t head_dim) { return head_dim <= 64 ? 2048 : 1024; }
 constexpr int32_t kMinChunksPerWave = 4;
+// The workgroup stream kernel launches one workgroup per compute unit of an
+// MI355X, fewer when a workgroup would get under this many chunks.
+constexpr int32_t kWgGroupTarget = 256;
+constexpr int32_t kMinChunksPerGroup = 32;
 
 struct Plan {
   bool ok;
@@ -52,6 +56,8 @@ struct Plan {
   bool balanced;
   int waves;         // partitioned kernel: waves per workgroup
   int stream_waves;  // stream kernel: wavefronts launched
+  int wg_groups;     // workgroup stream kernel: workgroups launched
+  int wg_windows;    // and windows per workgroup the workspace has slots for
   // workspace: [counters | partition outputs | (max, sum) pairs]
   size_t counter_bytes, part_out_offset, part_ml_offset, workspace_bytes;
 };
@@ -70,7 +76,8 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
     return p;
   if (d->out_dtype != PKV_DTYPE_BF16 && d->out_dtype != PKV_DTYPE_F32) return p;
   if (d->kernel != PKV_KERNEL_AUTO && d->kernel != PKV_KERNEL_MFMA &&
-      d->kernel != PKV_KERNEL_GENERIC && d->kernel != PKV_KERNEL_STREAM)
+      d->kernel != PKV_KERNEL_GENERIC && d->kernel != PKV_KERNEL_STREAM &&
+      d->kernel != PKV_KERNEL_STREAM_WG)
     return p;
   if (d->waves_per_group != 0 && d->waves_per_group != 1 && d->waves_per_group != 2 &&
       d->waves_per_group != 4)
@@ -87,10 +94,37 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
   const bool mfma_ok =
       pkv::mfma_shape_supported(d->head_dim, block_size, p.group, p.partition);
   const bool generic_ok = pkv::generic_shape_supported(d->head_dim, block_size, p.group);
+  const size_t units = static_cast<size_t>(d->num_seqs) * d->num_kv_heads;
+  // chunks the call can hold at most
+  const int64_t chunk_bound =
+      static_cast<int64_t>(units) * ((static_cast<int64_t>(d->max_seq_len) + 31) / 32);
+  // The workgroup stream kernel's launch: workgroups, and the windows each
+  // walks when the chunk bound exceeds what its LDS holds at once.
+  if (stream_ok) {
+    const int nw = pkv::wg_waves_per_group(d->head_dim);
+    int64_t groups = d->stream_waves > 0 ? (d->stream_waves + nw - 1) / nw : 0;
+    if (groups == 0) {
+      groups = (chunk_bound + kMinChunksPerGroup - 1) / kMinChunksPerGroup;
+      if (groups > kWgGroupTarget) groups = kWgGroupTarget;
+      if (groups < 1) groups = 1;
+    }
+    const pkv::WgLayout lay = pkv::wg_layout(d->head_dim, block_size, p.group, d->num_seqs, 1);
+    if (lay.capacity >= 1) {
+      const int64_t per_group = (chunk_bound + groups - 1) / groups;
+      const int64_t windows = per_group <= lay.capacity ? 1 : (per_group + lay.capacity - 1) / lay.capacity;
+      p.wg_groups = static_cast<int>(groups);
+      p.wg_windows = static_cast<int>(windows);
+    }
+  }
+  const bool wg_ok = stream_ok && p.wg_groups > 0;
   switch (d->kernel) {
     case PKV_KERNEL_STREAM:
       if (!stream_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
       p.family = kStream;
+      break;
+    case PKV_KERNEL_STREAM_WG:
+      if (!wg_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
+      p.family = kStreamWg;
       break;
     case PKV_KERNEL_MFMA:
       if (!mfma_ok) return (p.status = PKV_ERR_UNSUPPORTED, p);
@@ -101,7 +135,10 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
       p.family = kGeneric;
       break;
     default:
-      if (d->partition_size == 0 && stream_ok)
+      // the workgroup kernel when one window per workgroup holds the call
+      if (d->partition_size == 0 && wg_ok && p.wg_windows == 1)
+        p.family = kStreamWg;
+      else if (d->partition_size == 0 && stream_ok)
         p.family = kStream;
       else if (mfma_ok)
         p.family = kMfma;
@@ -110,12 +147,10 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
       else
         return (p.status = PKV_ERR_UNSUPPORTED, p);
   }
-  const size_t units = static_cast<size_t>(d->num_seqs) * d->num_kv_heads;
   const size_t counter_bytes = round_up(units * sizeof(uint32_t), kAlign);
-  if (p.family == kStream) {
-    // chunks the call can hold at most, and the wavefronts to share them
-    const int64_t chunk_bound =
-        static_cast<int64_t>(units) * ((static_cast<int64_t>(d->max_seq_len) + 31) / 32);
+  if (p.family == kStream || p.family == kStreamWg) {
+    // wavefronts (stream kernel) or windows (workgroup kernel) that share the
+    // chunks: each can publish one piece more than there are units
     int64_t wv = d->stream_waves;
     if (wv == 0) {
       wv = (chunk_bound + kMinChunksPerWave - 1) / kMinChunksPerWave;
@@ -126,7 +161,9 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
     p.stream_waves = static_cast<int>(wv);
     p.num_partitions = 1;
     // [counters | per-piece (acc) slots | per-piece (max, sum) slots]
-    const size_t slots = units + static_cast<size_t>(p.stream_waves);
+    const size_t slots =
+        units + (p.family == kStream ? static_cast<size_t>(p.stream_waves)
+                                     : static_cast<size_t>(p.wg_groups) * p.wg_windows);
     p.counter_bytes = counter_bytes;
     p.part_out_offset = p.counter_bytes;
     p.part_ml_offset = p.part_out_offset +
@@ -188,6 +225,17 @@ size_t pkv_decode_workspace_zeroed_bytes(const pkv_decode_dims* dims, int32_t bl
   return p.counter_bytes;
 }
 
+int32_t pkv_decode_plan_kernel(const pkv_decode_dims* dims, int32_t block_size) {
+  const Plan p = plan_decode(dims, block_size);
+  if (!p.ok) return -1;
+  switch (p.family) {
+    case kStreamWg: return PKV_KERNEL_STREAM_WG;
+    case kStream: return PKV_KERNEL_STREAM;
+    case kMfma: return PKV_KERNEL_MFMA;
+    default: return PKV_KERNEL_GENERIC;
+  }
+}
+
 }  // extern "C"
 
 namespace {
@@ -245,7 +293,7 @@ pkv_status decode_impl(const void* q, const void* k_new, const void* v_new, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* kc_w = static_cast<uint16_t*>(const_cast<void*>(k_cache));
   uint16_t* vc_w = static_cast<uint16_t*>(const_cast<void*>(v_cache));
-  if (append && p.family == kStream) {
+  if (append && (p.family == kStream || p.family == kStreamWg)) {
     // one launch: the wavefront that folds a unit's last chunk writes the new
     // token and uses it in place of the slot's old contents
     a.prm.k_new = static_cast<const uint16_t*>(k_new);
@@ -261,6 +309,8 @@ pkv_status decode_impl(const void* q, const void* k_new, const void* v_new, cons
   }
   switch (p.family) {
     case kStream: return hip_status(pkv::launch_decode_stream(a, p.stream_waves, s));
+    case kStreamWg:
+      return hip_status(pkv::launch_decode_wg(a, p.wg_groups, p.wg_windows, s));
     case kMfma: return hip_status(pkv::launch_decode_mfma(a, p.waves, s));
     default: return hip_status(pkv::launch_decode_generic(a, s));
   }

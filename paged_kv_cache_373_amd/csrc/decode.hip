@@ -31,86 +31,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "chunk.h"
 #include "internal.h"
 
 namespace pkv {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-
-// A running maximum is only raised when a chunk's maximum exceeds it by more
-// than this many powers of two.  Until then probabilities are formed against
-// the stale maximum and stay <= 2^8, which fp32 sums hold exactly as well as
-// values <= 1; the final division by the same-based sum makes the result
-// identical in exact arithmetic.  Rescaling the accumulators (a cross-lane
-// exchange) therefore happens a handful of times per partition, not per chunk.
-constexpr float kRescaleThreshold = 8.0f;
-
-// 32-token chunks each wavefront of the matrix-core kernels keeps in flight.
-#ifndef PKV_PIPELINE_DEPTH
-#define PKV_PIPELINE_DEPTH 2
-#endif
-constexpr int kDepth = PKV_PIPELINE_DEPTH;
-
-__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
-__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-  // v_cvt_pk_bf16_f32 rounds to nearest even
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Device-coherent accesses for data that workgroups hand to each other inside
-// one launch (split-KV partials): atomic at agent scope, so each access is
-// coherent across the chip's L2 caches by itself and no cache-wide write-back
-// or invalidation is needed.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Reads of partials through a buffer resource with the device-coherence cache
-// policy (the same bit an agent-scope atomic load carries).  Unlike atomic
-// loads the compiler keeps many of these in flight at once, which is what a
-// merge over many partials needs.  Offsets are in bytes and stay below
-// `bytes`; the resource's fourth word is the raw 32-bit data format of gfx9.
-struct CoherentReader {
-  static constexpr int kRsrcWord3 = 0x00020000;
-  static constexpr int kDeviceCoherent = 16;  // SC1
-  __amdgpu_buffer_rsrc_t rsrc;
-  __device__ CoherentReader(const void* base, uint32_t bytes)
-      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                               kRsrcWord3)) {}
-  __device__ float f32(uint32_t off) const {
-    return __builtin_bit_cast(float,
-                              __builtin_amdgcn_raw_buffer_load_b32(rsrc, off, 0, kDeviceCoherent));
-  }
-  __device__ f32x4_t f32x4(uint32_t off) const {
-    return __builtin_bit_cast(f32x4_t,
-                              __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kDeviceCoherent));
-  }
-};
-
-__device__ __forceinline__ void store_out(void* out, size_t idx, float v, int out_f32) {
-  if (out_f32)
-    static_cast<float*>(out)[idx] = v;
-  else
-    static_cast<uint16_t*>(out)[idx] = float_to_bf16_bits(v);
-}
 
 // Finishes one (sequence, q head) row of a vector-kernel partition: either the
 // final output (single partition) or the partition's (o_r, ln Z_r).  `m2` is
@@ -128,165 +53,6 @@ __device__ __forceinline__ void write_partition_result(const DecodeParams& prm, 
     if (d == 0) prm.part_lse[row * prm.num_partitions + p] = (m2 + __log2f(den)) * kLn2;
   }
 }
-
-// ---------------------------------------------------------------------------
-// The matrix-core chunk step shared by decode_stream and decode_mfma.
-//
-// A wavefront consumes a KV head's tokens 32 at a time (a "chunk": 1, 2 or 4
-// physical blocks at B = 32, 16, 8).  Lane roles (lane = 16 c + r, c in 0..3,
-// r in 0..15):
-//   QK^T   S^T[t][g] = sum_d K[t][d] Q[g][d] as two 16x16x32 MFMAs per 16-token
-//          half u of the chunk and per 32-wide slice of d.
-//          A operand (K): lane (c, r) holds 8 dims [32 hs + 8 c, +8) of token
-//          tok(u, r) = 8 (r / 4) + 4 u + r % 4 (one 16-byte load).
-//          B operand (Q): lane (c, r) holds the same 8 dims of query head g = r
-//          (zero for r >= G).
-//          Result: lane (c, g) holds scores of tokens 8 c + 4 u + i, i = 0..3.
-//   P.V    O[g][d] = sum_t P[g][t] V[t][d] as one 16x16x32 MFMA per 16-wide
-//          slice of d over the whole chunk.
-//          A operand (P): lane (c, g) holds P[g][8 c + e], e = 4 u + i, which
-//          is exactly the QK^T result layout: no data moves between lanes.
-//          B operand (V): lane (c, r) holds tokens 8 c .. 8 c + 7 of feature
-//          16 nt + r; in the transposed V tile this is one 16-byte load.
-//          A third MFMA against a ones operand sums P per head (the softmax
-//          denominator) from the same bf16-rounded P the numerator uses.
-//   Result rows: lane (c, r) holds O[g = 4 c + i][16 nt + r].
-// Every K load instruction covers 64 contiguous bytes of each of 16 token
-// rows; every V load instruction covers whole 32-byte token runs of 16
-// feature rows of one or two tiles, so a chunk's loads touch only the bytes
-// of its blocks, each once.
-template <int D, int BS>
-struct Mfma {
-  static_assert(D % 32 == 0 && D <= 128, "head_dim");
-  static_assert(BS == 8 || BS == 16 || BS == 32, "block_size");
-  static constexpr int HS = D / 32;                  // 32-wide slices of d (QK^T k-steps)
-  static constexpr int NT = D / 16;                  // 16-wide slices of d (P.V n-tiles)
-  static constexpr int NB = BS >= 32 ? 1 : 32 / BS;  // physical blocks per chunk
-  static constexpr size_t kTile = static_cast<size_t>(BS) * D;  // elements per (block, head)
-
-  struct Regs {  // one chunk's operands
-    bf16x8_t k[2][HS];
-    bf16x8_t v[NT];
-  };
-  struct State {  // online softmax of the G query heads of one KV head
-    float m2;        // running max of head g = r, base-2 units
-    f32x4_t acc[NT];
-    f32x4_t lsum;
-    __device__ void reset() {
-      m2 = -INFINITY;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      lsum = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  struct Lane {  // lane-constant address parts
-    int kj[2], koff[2], vj, voff;
-    __device__ explicit Lane(int c, int r) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int tok = 8 * (r >> 2) + 4 * u + (r & 3);
-        kj[u] = tok / BS;
-        koff[u] = (tok % BS) * D + 8 * c;
-      }
-      vj = (8 * c) / BS;
-      voff = r * BS + (8 * c) % BS;
-    }
-  };
-
-  // Query group of KV head `kvh` of sequence b as the QK^T B operand.
-  static __device__ void load_q(const uint16_t* q, int Hq, int G, int b, int kvh, int c, int r,
-                                bf16x8_t (&qop)[HS]) {
-    const uint16_t* qrow =
-        q + (static_cast<size_t>(b) * Hq + kvh * G + (r < G ? r : 0)) * D + 8 * c;
-#pragma unroll
-    for (int hs = 0; hs < HS; ++hs) qop[hs] = load_bf16x8(qrow + 32 * hs);
-    if (r >= G) {
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) qop[hs] = bf16x8_t{};
-    }
-  }
-
-  // Issues the loads of one chunk whose NB (block, head) tiles start at the
-  // element offsets `base` (wave-uniform).
-  static __device__ void load(const uint16_t* k_cache, const uint16_t* v_cache,
-                              const size_t (&base)[NB], const Lane& ln, Regs& x) {
-    auto pick = [&](int j) {
-      size_t v = base[0];
-#pragma unroll
-      for (int jj = 1; jj < NB; ++jj) v = (j == jj) ? base[jj] : v;
-      return v;
-    };
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint16_t* kp = k_cache + pick(ln.kj[u]) + ln.koff[u];
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) x.k[u][hs] = load_bf16x8(kp + 32 * hs);
-    }
-    const uint16_t* vp = v_cache + pick(ln.vj) + ln.voff;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) x.v[nt] = load_bf16x8(vp + 16 * nt * BS);
-  }
-
-  // Folds one chunk into the state.  Tokens valid .. 31 of the chunk
-  // (valid in 1..32, wave-uniform) lie past the sequence: their scores are
-  // selected to -inf and their V rows to 0, so whatever those slots hold
-  // (NaN included) never reaches the result.
-  static __device__ void step(const bf16x8_t (&qop)[HS], Regs& x, int valid, float sl, int c,
-                              State& st) {
-    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int hs = 0; hs < HS; ++hs) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[0][hs], qop[hs], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[1][hs], qop[hs], s1, 0, 0, 0);
-    }
-    // xs[e]: score of token 8 c + e in base-2 units, e = 4 u + i
-    float xs[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xs[i] = s0[i] * sl;
-      xs[4 + i] = s1[i] * sl;
-    }
-    const bool tail = valid < 32;   // wave-uniform
-    const int lv = valid - 8 * c;   // tokens of this lane group still in range
-    if (tail) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xs[e] = (e < lv) ? xs[e] : -INFINITY;
-    }
-    float cm = xs[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, xs[e]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
-    // every lane of head g now holds the chunk maximum of head g
-    if (__ballot(cm > st.m2 + kRescaleThreshold) != 0) {
-      const float mn = fmaxf(st.m2, cm);
-      const float alpha = fast_exp2(st.m2 - mn);  // 0 on the first chunk (m2 = -inf)
-      st.m2 = mn;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = __shfl(alpha, 4 * c + i);  // factor of head 4 c + i
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st.acc[nt][i] *= a;
-        st.lsum[i] *= a;
-      }
-    }
-    bf16x8_t pa;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(fast_exp2(xs[e] - st.m2));
-    if (tail) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          x.v[nt][e] = (e < lv) ? x.v[nt][e] : static_cast<__bf16>(0.f);
-    }
-    const bf16x8_t ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, x.v[nt], st.acc[nt], 0, 0, 0);
-    st.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, st.lsum, 0, 0, 0);
-  }
-};
 
 // ---------------------------------------------------------------------------
 // Stream kernel.
@@ -344,39 +110,10 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
   const int r = lane & 15;
 
   // 1. Lengths, and the exclusive prefix of per-sequence chunk counts.
-  for (int b = tid; b < S; b += NTH) s_len[b] = seq_lens[b];
-  __syncthreads();
-  const int per = (S + NTH - 1) / NTH;  // thread tid sums sequences [tid per, tid per + per)
-  int mine = 0;
-  for (int j = 0; j < per; ++j) {
-    const int b = tid * per + j;
-    if (b < S) mine += (s_len[b] + 31) >> 5;
-  }
-  int incl = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) s_wsum[w] = incl;
-  __syncthreads();
-  int run = incl - mine;
-  for (int ww = 0; ww < w; ++ww) run += s_wsum[ww];
-  for (int j = 0; j < per; ++j) {
-    const int b = tid * per + j;
-    if (b < S) {
-      s_pre[b] = run;
-      run += (s_len[b] + 31) >> 5;
-    }
-  }
-  if (tid == NTH - 1) s_pre[S] = run;
-  __syncthreads();
+  chunk_prefix<NTH>(seq_lens, S, s_len, s_pre, s_wsum, tid);
 
   // 2. Sequences with no tokens get a zero output row.
-  for (int b = blockIdx.x; b < S; b += gridDim.x)
-    if (s_len[b] == 0)
-      for (int e = tid; e < Hq * D; e += NTH)
-        store_out(prm.out, static_cast<size_t>(b) * Hq * D + e, 0.f, prm.out_f32);
+  zero_empty_rows<D, NTH>(prm, s_len, tid);
 
   // 3. This wavefront's share of the chunks.  (No barrier below this point:
   // the wavefronts of a workgroup are independent from here on.)
@@ -636,56 +373,13 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
         // valid - 1): its K/V come from k_new/v_new into the operand registers
         // (the cache slot was read before it is written), then go to the slot.
         const int tn = valid - 1;
-        const int hh = __builtin_amdgcn_readlane(chd, i);
-        const size_t src = (static_cast<size_t>(__builtin_amdgcn_readlane(cb, i)) * Hkv + hh) * D;
-        const int un = (tn & 7) >> 2;            // K operand half holding the token
-        const int rn = 4 * (tn >> 3) + (tn & 3); // and its lane row
-        const int cn = tn >> 3;                  // V operand lane group holding the token
-        const int en = tn & 7;                   // and its element
-        bf16x8_t kn[HS];
-#pragma unroll
-        for (int hs = 0; hs < HS; ++hs) kn[hs] = load_bf16x8(prm.k_new + src + 32 * hs + 8 * c);
-        uint16_t vn[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) vn[nt] = prm.v_new[src + 16 * nt + r];
-        __builtin_amdgcn_s_waitcnt(0);
-        const bool in0 = (r == rn) && (un == 0);
-        const bool in1 = (r == rn) && (un == 1);
-#pragma unroll
-        for (int hs = 0; hs < HS; ++hs) {
-          const u32x4_t nk = __builtin_bit_cast(u32x4_t, kn[hs]);
-          const u32x4_t o0 = __builtin_bit_cast(u32x4_t, x.k[0][hs]);
-          const u32x4_t o1 = __builtin_bit_cast(u32x4_t, x.k[1][hs]);
-          u32x4_t r0, r1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            r0[e] = in0 ? nk[e] : o0[e];
-            r1[e] = in1 ? nk[e] : o1[e];
-          }
-          x.k[0][hs] = __builtin_bit_cast(bf16x8_t, r0);
-          x.k[1][hs] = __builtin_bit_cast(bf16x8_t, r1);
-        }
-        if (c == cn) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              x.v[nt][e] = (e == en) ? __builtin_bit_cast(__bf16, vn[nt]) : x.v[nt][e];
-        }
-        // slot of the new token: block tn / BS of the chunk, offset tn % BS
+        // the chunk's block holding position tn
         int blk = __builtin_amdgcn_readlane(ent[0], i);
 #pragma unroll
         for (int j = 1; j < NB; ++j)
           blk = (tn / BS == j) ? __builtin_amdgcn_readlane(ent[j], i) : blk;
-        const size_t tile = (static_cast<size_t>(blk) * Hkv + hh) * M::kTile;
-        const int off = tn % BS;
-        if (lane < 4 * HS) {  // K row: HS x 4 pieces of 16 bytes
-          const int hs = lane >> 2, cc4 = lane & 3;
-          *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 32 * hs + 8 * cc4) =
-              *reinterpret_cast<const u32x4_t*>(prm.k_new + src + 32 * hs + 8 * cc4);
-        }
-        for (int d = lane; d < D; d += 64) prm.v_cache_w[tile + static_cast<size_t>(d) * BS + off] =
-            prm.v_new[src + d];
+        patch_new_token<D, BS>(prm, x, valid, __builtin_amdgcn_readlane(cb, i),
+                               __builtin_amdgcn_readlane(chd, i), blk, lane);
       }
       M::step(sl8.q, x, valid, sl, c, st);
       if (fl & 2) finish_piece(__builtin_amdgcn_readlane(clc, i));

@@ -1,0 +1,515 @@
+// decode_wg.hip - the workgroup stream decode kernel for gfx950 (CDNA4).
+//
+// Sources (by title and section):
+//   [ITH] iThome ithelp article 10405755 on PagedAttention, section
+//         "PagedAttention 的核心想法": attention over a sequence's tokens is
+//         unchanged; the kernel finds each token's K,V through the block table.
+//   [PU]  Fanyi Pu, "Infra: PagedAttention", section "按 Block 分配": softmax
+//         spans every visible token; segment results (o, max, Z) merge by
+//         o = (Z1 o1 + Z2 o2) / (Z1 + Z2) after rescaling to a common maximum,
+//         and segments need not coincide with physical blocks.
+//
+// The work of a call is the same as the stream kernel's: every (sequence b,
+// KV head h) unit u = b Hkv + h cut into n_b = ceil(T_b / 32) chunks of 32
+// tokens, C chunks in unit order.  It is dealt out in equal contiguous
+// windows, but here a window belongs to a whole workgroup - all the
+// wavefronts one compute unit holds - rather than to one wavefront:
+//
+//   * Inside a window the wavefronts take chunks one at a time from a counter
+//     in LDS, so a wavefront that the hardware serves more slowly simply
+//     takes fewer; the workgroup's wavefronts finish together.
+//   * Each chunk is folded on its own (a fresh online softmax) and leaves its
+//     (max, sum, accumulator) in an LDS slot of its own.  Once every chunk of
+//     the window is in, the workgroup merges each unit's slots in chunk order
+//     by the rescaled segment rule, one wavefront per unit.  Which wavefront
+//     folded which chunk therefore never changes a result bit.
+//   * A unit that lies wholly in the window is written to the output there.
+//     A unit cut by a window edge is published as a piece (the window's part
+//     of it) and counted; the last piece to arrive merges all of the unit's
+//     pieces in window order, as in the stream kernel.
+//
+// A window holds at most `capacity` chunks (the LDS slots).  When the call's
+// chunks need more, each workgroup walks several windows in turn, with a
+// barrier between them.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "chunk.h"
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+// Words (4 bytes) of LDS per window chunk besides its state: the chunk
+// record (kRecBase + NB words) and a unit record (kUnitWords).
+constexpr int kRecBase = 5;  // sequence, KV head, chunk of unit, valid | flags << 8, unit record
+constexpr int kUnitWords = 3;  // first window position, chunks in window, whole
+constexpr int kMiscWords = 4;  // chunk counter
+
+template <int D, int BS, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
+    decode_wg(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+              const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+              const int32_t* __restrict__ seq_lens, const DecodeParams prm, const WgLayout lay) {
+  using M = Mfma<D, BS>;
+  using Regs = typename M::Regs;
+  constexpr int NB = M::NB;
+  constexpr int HS = M::HS;
+  constexpr int NT = M::NT;
+  constexpr int DEPTH = kDepth;
+  constexpr int NTH = NW * 64;
+  constexpr int kBlocksPerChunk = 32 / BS;
+  constexpr int DS = kRecBase + NB;  // words per chunk record
+  constexpr int E4 = D / 4;          // float4s per head in a state slot
+
+  extern __shared__ __align__(16) int lds[];
+  int* s_len = lds + lay.off_len;
+  int* s_pre = lds + lay.off_pre;
+  int* s_wsum = lds + lay.off_wsum;
+  int* s_misc = lds + lay.off_misc;
+  int* s_rec = lds + lay.off_rec;
+  int* s_unit = lds + lay.off_unit;
+  float* s_acc = reinterpret_cast<float*>(lds + lay.off_acc);  // [capacity][G][16][NT]
+  float* s_ml = reinterpret_cast<float*>(lds + lay.off_ml);    // [capacity][G][max, sum]
+
+  const int S = prm.num_seqs;
+  const int Hkv = prm.num_kv_heads;
+  const int Hq = prm.num_q_heads;
+  const int G = prm.group;
+  const int MB = prm.max_blocks_per_seq;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane >> 4;
+  const int r = lane & 15;
+
+  // 1. Lengths and the chunk prefix; the windows of this workgroup.
+  chunk_prefix<NTH>(seq_lens, S, s_len, s_pre, s_wsum, tid);
+  const int64_t C = static_cast<int64_t>(Hkv) * s_pre[S];
+  const int64_t NWG = gridDim.x;
+  const int64_t per_group = (C + NWG - 1) / NWG;
+  const int64_t wpg = per_group <= lay.capacity ? 1 : (per_group + lay.capacity - 1) / lay.capacity;
+  if (wpg > lay.max_windows) {
+    // More chunks than the bound the launch was sized for (some T_b above
+    // max_seq_len): every output row becomes NaN.
+    for (int b = blockIdx.x; b < S; b += gridDim.x)
+      for (int e = tid; e < Hq * D; e += NTH)
+        store_out(prm.out, static_cast<size_t>(b) * Hq * D + e, NAN, prm.out_f32);
+    return;
+  }
+  zero_empty_rows<D, NTH>(prm, s_len, tid);
+  const int64_t NWIN = NWG * wpg;
+  const int64_t NWeff = C < NWIN ? C : NWIN;  // windows that hold chunks
+
+  const typename M::Lane ln(c, r);
+  const float sl = prm.scale_log2;
+  const size_t blk_stride = static_cast<size_t>(Hkv) * M::kTile;
+  struct Slot {  // one ring entry: a chunk's K/V operands, its unit's query group, its position
+    Regs x;
+    bf16x8_t q[HS];
+    int pos;
+  };
+
+  // Sequence holding global chunk cc: the largest lo with Hkv * s_pre[lo] <= cc.
+  auto seq_of = [&](int64_t cc) {
+    int lo = 0, hi = S;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (static_cast<int64_t>(Hkv) * s_pre[mid] <= cc)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return lo;
+  };
+
+  for (int64_t k = 0; k < wpg; ++k) {
+    const int64_t x = static_cast<int64_t>(blockIdx.x) * wpg + k;  // window id
+    if (x >= NWeff) break;
+    const int64_t ws = x * C / NWeff;
+    const int n = static_cast<int>((x + 1) * C / NWeff - ws);
+    if (k > 0) __syncthreads();  // the previous window's slots are merged
+
+    // 2. The window's chunk records and unit records.  A unit's record sits
+    // at the window position of its first chunk there (its chunks are
+    // consecutive, so that is t - lc, or 0 for a unit begun before the window).
+    {
+      for (int t = tid; t < n; t += NTH) {
+        const int64_t cc = ws + t;
+        const int b = seq_of(cc);
+        const int T = s_len[b];
+        const int nb = (T + 31) >> 5;
+        const int rem = static_cast<int>(cc - static_cast<int64_t>(Hkv) * s_pre[b]);
+        const int h = rem / nb;
+        const int lc = rem - h * nb;
+        const int valid = min(32, T - 32 * lc);
+        const int lu = t - lc > 0 ? t - lc : 0;
+        int* rec = s_rec + t * DS;
+        rec[0] = b;
+        rec[1] = h;
+        rec[2] = lc;
+        rec[3] = valid | ((lc == nb - 1 ? 4 : 0) << 8);
+        rec[4] = lu;
+        const int last_blk = (T + BS - 1) / BS - 1;
+        const int32_t* row = block_tables + static_cast<size_t>(b) * MB;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) rec[kRecBase + j] = row[min(lc * kBlocksPerChunk + j, last_blk)];
+        if (t == 0 || lc == 0) {  // the unit's first chunk in the window
+          int* ur = s_unit + lu * kUnitWords;
+          ur[0] = t;
+          ur[1] = min(nb - lc, n - t);
+          ur[2] = (lc == 0 && nb <= n - t) ? 1 : 0;
+        }
+      }
+      if (tid == 0) s_misc[0] = 0;  // chunk counter
+      __syncthreads();
+    }
+    // Windows holding the first and the last chunk of unit (b, h).
+    auto unit_span = [&](int b, int h, int64_t& gf, int64_t& gl) {
+      const int nb = (s_len[b] + 31) >> 5;
+      const int64_t cu0 = static_cast<int64_t>(Hkv) * s_pre[b] + static_cast<int64_t>(h) * nb;
+      gf = ((cu0 + 1) * NWeff - 1) / C;
+      gl = ((cu0 + nb) * NWeff - 1) / C;
+    };
+
+    auto grab = [&]() {
+      int j = 0;
+      if (lane == 0)
+        j = __hip_atomic_fetch_add(s_misc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      return __builtin_amdgcn_readfirstlane(j);
+    };
+    auto issue = [&](int pos, Slot& sl8) {
+      const int* rec = s_rec + pos * DS;
+      const int b = __builtin_amdgcn_readfirstlane(rec[0]);
+      const int hh = __builtin_amdgcn_readfirstlane(rec[1]);
+      const size_t head_off = static_cast<size_t>(hh) * M::kTile;
+      size_t base[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        base[j] = static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[kRecBase + j])) *
+                      blk_stride + head_off;
+      M::load(k_cache, v_cache, base, ln, sl8.x);
+      M::load_q(q, Hq, G, b, hh, c, r, sl8.q);
+      sl8.pos = pos;
+    };
+
+    // The merged state of unit (b, hh) over its k window chunks from
+    // position p0, for float4 e of the [G][16][NT] slot layout (head gh).
+    // Slots are read eight at a time (all eight reads in flight) and folded
+    // against a running maximum; the batches and the order within them
+    // depend on kk alone.
+    auto merge_slots = [&](int p0, int kk, int e, int gh, float& mx, float& den, f32x4_t& num) {
+      mx = -INFINITY;
+      den = 0.f;
+      num = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < kk; j0 += 8) {
+        float2 ml[8];
+        f32x4_t a[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int p = p0 + min(j0 + t, kk - 1);
+          ml[t] = *reinterpret_cast<const float2*>(s_ml + (p * G + gh) * 2);
+          a[t] = *reinterpret_cast<const f32x4_t*>(s_acc + static_cast<size_t>(p) * G * D + 4 * e);
+        }
+        float bm = ml[0].x;
+#pragma unroll
+        for (int t = 1; t < 8; ++t) bm = (j0 + t < kk) ? fmaxf(bm, ml[t].x) : bm;
+        const float mn = fmaxf(mx, bm);
+        const float fo = fast_exp2(mx - mn);  // 0 before the first batch
+        den *= fo;
+        num *= fo;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if (j0 + t < kk) {
+            const float f = fast_exp2(ml[t].x - mn);
+            den += f * ml[t].y;
+            num += f * a[t];
+          }
+        }
+        mx = mn;
+      }
+    };
+    // Output row features of float4 e: d = 16 nt + rr for nt = 4 n4 .. 4 n4 + 3.
+    auto store_row4 = [&](size_t row, int e, int gh, const f32x4_t& v) {
+      const int rem = e - gh * E4;
+      const int rr = rem / (NT / 4);
+      const int n4 = rem - rr * (NT / 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        store_out(prm.out, row * D + 16 * (4 * n4 + t) + rr, v[t], prm.out_f32);
+    };
+    // All pieces of unit (b, hh) - windows gf .. gl, published and counted -
+    // merged in window order into the output.
+    auto merge_pieces = [&](int b, int hh, int64_t gf, int64_t gl) {
+      const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
+      const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hh) * G;
+      const int kp = static_cast<int>(gl - gf + 1);
+      const CoherentReader racc(prm.part_out + (u + gf) * G * D,
+                                static_cast<uint32_t>(kp * G * D * sizeof(float)));
+      const CoherentReader rml(prm.part_ml + (u + gf) * G * 2,
+                               static_cast<uint32_t>(kp * G * 2 * sizeof(float)));
+      for (int e = lane; e < G * E4; e += 64) {
+        const int gh = e / E4;
+        float mx = -INFINITY, den = 0.f;
+        f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+        for (int j0 = 0; j0 < kp; j0 += 8) {  // eight pieces' loads in flight at a time
+          f32x4_t a[8];
+          float pm[8], pl[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int j = min(j0 + t, kp - 1);
+            a[t] = racc.f32x4(static_cast<uint32_t>((j * G * D + 4 * e) * sizeof(float)));
+            pm[t] = rml.f32(static_cast<uint32_t>(((j * G + gh) * 2) * sizeof(float)));
+            pl[t] = rml.f32(static_cast<uint32_t>(((j * G + gh) * 2 + 1) * sizeof(float)));
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            if (j0 + t < kp) {
+              const float mn = fmaxf(mx, pm[t]);
+              const float fo = fast_exp2(mx - mn);  // 0 for the first piece
+              const float fj = fast_exp2(pm[t] - mn);
+              den = den * fo + pl[t] * fj;
+              num = num * fo + a[t] * fj;
+              mx = mn;
+            }
+          }
+        }
+        store_row4(row0 + gh, e, gh, num * (1.0f / den));
+      }
+    };
+    // Merges unit lu's kk window slots: the output when the unit is whole in
+    // the window, else its piece, published to slot u + x.
+    auto merge_unit = [&](int lu, int kk, int whole, int b, int hh) {
+      const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hh) * G;
+      const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
+      float* pacc = prm.part_out + (u + x) * G * D;  // [G][16][NT]
+      float* pml = prm.part_ml + (u + x) * G * 2;    // [G][max, sum]
+      for (int e = lane; e < G * E4; e += 64) {
+        const int gh = e / E4;
+        float mx, den;
+        f32x4_t num;
+        merge_slots(lu, kk, e, gh, mx, den, num);
+        if (whole) {
+          store_row4(row0 + gh, e, gh, num * (1.0f / den));
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) store_coherent(pacc + 4 * e + t, num[t]);
+          if (e == gh * E4) {
+            store_coherent(pml + gh * 2, mx);
+            store_coherent(pml + gh * 2 + 1, den);
+          }
+        }
+      }
+    };
+    // Folds the chunk in `sl8` into its LDS slot.
+    auto consume = [&](Slot& sl8) {
+      const int pos = sl8.pos;
+      const int* rec = s_rec + pos * DS;
+      const int vf = __builtin_amdgcn_readfirstlane(rec[3]);
+      const int valid = vf & 255;
+      if (((vf >> 8) & 4) && prm.k_new != nullptr) {
+        // the unit's last chunk holds the new token of a fused decode step
+        const int tn = valid - 1;
+        patch_new_token<D, BS>(prm, sl8.x, valid, __builtin_amdgcn_readfirstlane(rec[0]),
+                               __builtin_amdgcn_readfirstlane(rec[1]),
+                               __builtin_amdgcn_readfirstlane(rec[kRecBase + tn / BS]), lane);
+      }
+      typename M::State st;
+      st.reset();
+      M::step(sl8.q, sl8.x, valid, sl, c, st);
+      float* sa = s_acc + static_cast<size_t>(pos) * G * D;
+      float* sm = s_ml + static_cast<size_t>(pos) * G * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gh = 4 * c + i;
+        if (gh < G) {
+#pragma unroll
+          for (int n4 = 0; n4 < NT / 4; ++n4)
+            *reinterpret_cast<f32x4_t*>(sa + gh * D + r * NT + 4 * n4) =
+                f32x4_t{st.acc[4 * n4][i], st.acc[4 * n4 + 1][i], st.acc[4 * n4 + 2][i],
+                        st.acc[4 * n4 + 3][i]};
+          if (r == 0) sm[gh * 2 + 1] = st.lsum[i];
+        }
+      }
+      if (c == 0 && r < G) sm[r * 2] = st.m2;
+    };
+
+    // 3. The wavefronts take chunks until the window's are gone.  Every ring
+    // refill issues its loads (a chunk past the window re-reads the window's
+    // first chunk, which nobody folds) so the wait counts stay exact.
+    Slot ring[DEPTH];
+    int jr[DEPTH];
+#pragma unroll
+    for (int s = 0; s < DEPTH; ++s) {
+      jr[s] = grab();
+      issue(jr[s] < n ? jr[s] : 0, ring[s]);
+    }
+    // A wavefront's grabs rise, and it folds its chunks in grab order: once
+    // one lies past the window, so do all the ring's later entries.  (The
+    // ring is walked with constant indices so its registers stay put.)
+    static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
+    auto advance = [&](Slot& sl8, int& j) {
+      consume(sl8);
+      j = grab();
+      issue(j < n ? j : 0, sl8);
+    };
+    for (;;) {
+      if (jr[0] >= n) break;
+      advance(ring[0], jr[0]);
+      if constexpr (DEPTH > 1) {
+        if (jr[1] >= n) break;
+        advance(ring[1], jr[1]);
+      }
+      if constexpr (DEPTH > 2) {
+        if (jr[2] >= n) break;
+        advance(ring[2], jr[2]);
+      }
+    }
+
+    // 4. Every chunk of the window is in its slot: the wavefronts merge the
+    // window's units, one wavefront per unit.  The units cut by the window's
+    // edges (its first and its last) go to different wavefronts and are
+    // published first; the whole units follow, so the pieces' stores
+    // complete while that work goes on; then the published pieces are
+    // counted and the last piece of each unit merges them all.
+    __syncthreads();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int nunits = 0;
+    for (int p0 = 0; p0 < n; p0 += 64) {
+      const int p = p0 + lane;
+      nunits += __builtin_popcountll(__ballot(p < n && s_rec[p * DS + 4] == p));
+    }
+    auto owner = [&](int rank) { return rank == nunits - 1 ? NW - 1 : rank % (NW - 1); };
+    int npub = 0, pub_b[2] = {0, 0}, pub_h[2] = {0, 0};
+    for (int pass = 0; pass < 2; ++pass) {  // 0: cut units, 1: whole units
+      int rank = 0;
+      for (int p0 = 0; p0 < n; p0 += 64) {
+        const int p = p0 + lane;
+        uint64_t m = __ballot(p < n && s_rec[p * DS + 4] == p);
+        for (; m != 0; m &= m - 1, ++rank) {
+          const int lu = p0 + __builtin_ctzll(m);
+          if (owner(rank) != w) continue;
+          const int whole = __builtin_amdgcn_readfirstlane(s_unit[lu * kUnitWords + 2]);
+          if (whole != pass) continue;
+          const int kk = __builtin_amdgcn_readfirstlane(s_unit[lu * kUnitWords + 1]);
+          const int b = __builtin_amdgcn_readfirstlane(s_rec[lu * DS]);
+          const int hh = __builtin_amdgcn_readfirstlane(s_rec[lu * DS + 1]);
+          merge_unit(lu, kk, whole, b, hh);
+          if (!whole) {
+            if (npub < 2) {
+              pub_b[npub] = b;
+              pub_h[npub] = hh;
+            }
+            ++npub;
+          }
+        }
+      }
+    }
+    // (Only a window's first and last units can be cut, and they have
+    // different owners, so npub <= 1 here; two are handled all the same.)
+    if (npub > 0) {
+      __builtin_amdgcn_s_waitcnt(0);  // the pieces are visible before they are counted
+      for (int t = 0; t < npub && t < 2; ++t) {
+        const int b = t == 0 ? pub_b[0] : pub_b[1];
+        const int hh = t == 0 ? pub_h[0] : pub_h[1];
+        const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
+        uint32_t prev = 0;
+        if (lane == 0)
+          prev = __hip_atomic_fetch_add(prm.counters + u, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+        prev = __builtin_amdgcn_readfirstlane(prev);
+        int64_t gf, gl;
+        unit_span(b, hh, gf, gl);
+        if (prev == static_cast<uint32_t>(gl - gf)) {
+          merge_pieces(b, hh, gf, gl);
+          // every piece has been counted: leave the counter at zero for the next call
+          if (lane == 0)
+            __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+}
+
+// Allows an instantiation the LDS a workgroup may use beyond the default
+// dynamic allowance (once per process; repeated calls set the same value).
+template <int D, int BS, int NW>
+hipError_t allow_lds() {
+  static const hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&decode_wg<D, BS, NW>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kWgLdsBytes);
+  return e;
+}
+
+template <int D, int NW>
+hipError_t launch_wg_bs(const DecodeLaunch& a, int groups, const WgLayout& lay, size_t lds,
+                        hipStream_t stream) {
+  const dim3 grid(groups), block(NW * 64);
+  const hipError_t e = a.prm.block_size == 8    ? allow_lds<D, 8, NW>()
+                       : a.prm.block_size == 16 ? allow_lds<D, 16, NW>()
+                                                : allow_lds<D, 32, NW>();
+  if (e != hipSuccess) return e;
+  switch (a.prm.block_size) {
+    case 8:
+      decode_wg<D, 8, NW><<<grid, block, lds, stream>>>(a.q, a.k_cache, a.v_cache,
+                                                         a.block_tables, a.seq_lens, a.prm, lay);
+      break;
+    case 16:
+      decode_wg<D, 16, NW><<<grid, block, lds, stream>>>(a.q, a.k_cache, a.v_cache,
+                                                          a.block_tables, a.seq_lens, a.prm, lay);
+      break;
+    default:
+      decode_wg<D, 32, NW><<<grid, block, lds, stream>>>(a.q, a.k_cache, a.v_cache,
+                                                          a.block_tables, a.seq_lens, a.prm, lay);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int wg_waves_per_group(int head_dim) { return head_dim <= 64 ? 8 : 4; }
+
+WgLayout wg_layout(int head_dim, int block_size, int group, int num_seqs, int max_windows) {
+  WgLayout lay = {};
+  const int nb = block_size >= 32 ? 1 : 32 / block_size;
+  const int nw = wg_waves_per_group(head_dim);
+  auto up4 = [](int w) { return (w + 3) / 4 * 4; };
+  int w = 0;
+  lay.off_len = w;
+  w = up4(w + num_seqs);
+  lay.off_pre = w;
+  w = up4(w + num_seqs + 1);
+  lay.off_wsum = w;
+  w = up4(w + nw);
+  lay.off_misc = w;
+  w = up4(w + kMiscWords);
+  const int fixed = w;
+  const int per_chunk = kRecBase + nb + kUnitWords + group * head_dim + 2 * group;
+  int cap = (kWgLdsBytes / 4 - fixed - 3 * 4) / per_chunk;
+  if (cap > kWgMaxCapacity) cap = kWgMaxCapacity;
+  lay.capacity = cap;
+  lay.off_rec = w;
+  w = up4(w + cap * (kRecBase + nb));
+  lay.off_unit = w;
+  w = up4(w + cap * kUnitWords);
+  lay.off_acc = w;
+  w = up4(w + cap * group * head_dim);
+  lay.off_ml = w;
+  w = up4(w + cap * group * 2);
+  lay.words = w;
+  lay.max_windows = max_windows;
+  return lay;
+}
+
+hipError_t launch_decode_wg(const DecodeLaunch& a, int num_groups, int max_windows,
+                            hipStream_t stream) {
+  const WgLayout lay = wg_layout(a.prm.head_dim, a.prm.block_size, a.prm.group, a.num_seqs,
+                                 max_windows);
+  if (lay.capacity < 1) return hipErrorInvalidValue;
+  const size_t lds = static_cast<size_t>(lay.words) * 4;
+  return a.prm.head_dim == 64 ? launch_wg_bs<64, 8>(a, num_groups, lay, lds, stream)
+                              : launch_wg_bs<128, 4>(a, num_groups, lay, lds, stream);
+}
+
+}  // namespace pkv

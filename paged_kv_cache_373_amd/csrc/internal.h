@@ -61,6 +61,22 @@ hipError_t launch_decode_stream(const DecodeLaunch& a, int num_waves, hipStream_
 hipError_t launch_decode_mfma(const DecodeLaunch& a, int waves, hipStream_t stream);
 hipError_t launch_decode_generic(const DecodeLaunch& a, hipStream_t stream);
 
+// Workgroup stream kernel.  One workgroup per compute unit holds
+// wg_waves_per_group(head_dim) wavefronts; its LDS (dynamic shared memory) is
+// carved as below, in 4-byte words, with room for `capacity` chunks a window.
+constexpr int kWgLdsBytes = 160 * 1024;  // LDS a workgroup may use on gfx950
+constexpr int kWgMaxCapacity = 1024;     // chunks a window holds at most
+struct WgLayout {
+  int32_t capacity;     // chunks per window
+  int32_t max_windows;  // windows per workgroup the workspace has slots for
+  int32_t off_len, off_pre, off_wsum, off_misc, off_rec, off_unit, off_acc, off_ml;
+  int32_t words;        // total LDS words
+};
+int wg_waves_per_group(int head_dim);
+WgLayout wg_layout(int head_dim, int block_size, int group, int num_seqs, int max_windows);
+hipError_t launch_decode_wg(const DecodeLaunch& a, int num_groups, int max_windows,
+                            hipStream_t stream);
+
 // Split-KV merge.  With seq_lens != nullptr, row r = b * rows_per_seq + h
 // merges ceil(seq_lens[b] / partition_size) partitions and rows that have at
 // most one partition are skipped (their output was written directly);

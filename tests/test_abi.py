@@ -112,13 +112,73 @@ def test_workspace_size_rules_stream():
     slots = 16 + 8
     assert ws(d) == 256 + slots * 4 * 64 * 4 + slots * 4 * 2 * 4
     assert zb(d) == 256
-    assert ws(_dims()) == ws(d)  # AUTO with no partition size runs the stream kernel
     d2 = _dims(kernel=3, stream_waves=64)
     assert ws(d2) == 256 + (16 + 64) * 4 * 64 * 4 + (16 + 64) * 4 * 2 * 4
     assert ws(_dims(kernel=3, stream_waves=6)) == BAD  # not a multiple of 4
     assert ws(_dims(kernel=3, num_seqs=4096)) == BAD  # over the stream kernel's sequence limit
     assert ws(_dims(num_seqs=4096)) == 0  # AUTO falls back to one 256-token partition
     assert ws(_dims(kernel=3, head_dim=80)) == BAD
+
+
+def _wg_capacity(num_seqs, group, head_dim, block_size):
+    """Chunks one window of the workgroup kernel holds: 160 KiB of LDS less the
+    per-sequence arrays, over the per-chunk words (record, unit record, state)."""
+    up4 = lambda w: (w + 3) // 4 * 4
+    nw = 8 if head_dim <= 64 else 4
+    nb = 1 if block_size >= 32 else 32 // block_size
+    fixed = up4(num_seqs) + up4(num_seqs + 1) + up4(nw) + 4
+    per_chunk = 5 + nb + 3 + group * head_dim + 2 * group
+    return min((160 * 1024 // 4 - fixed - 12) // per_chunk, 1024)
+
+
+def test_workspace_size_rules_stream_wg():
+    # 2 sequences x 8 KV heads, up to 2 chunks each: 32 chunks, one workgroup
+    # (32 chunks per workgroup at least), one window: slots = 16 units + 1
+    d = _dims(kernel=4)
+    region = lambda n: (n + 255) // 256 * 256
+    assert ws(d) == 256 + region(17 * 4 * 64 * 4) + region(17 * 4 * 2 * 4)
+    assert zb(d) == 256
+    assert ws(_dims()) == ws(d)  # AUTO with no partition size runs this kernel
+    # stream_waves rounds up to whole workgroups of 8 wavefronts: 9 -> 2 groups
+    d2 = _dims(kernel=4, stream_waves=64)
+    assert ws(d2) == 256 + region((16 + 8) * 4 * 64 * 4) + region((16 + 8) * 4 * 2 * 4)
+    d3 = _dims(kernel=4, stream_waves=68)
+    assert ws(d3) == 256 + region((16 + 9) * 4 * 64 * 4) + region((16 + 9) * 4 * 2 * 4)
+    # batch 64 x 8 KV heads up to 2048 tokens: 32768 chunks over 256 workgroups
+    # is 128 per workgroup, within one window's capacity
+    cap = _wg_capacity(64, 4, 64, 16)
+    assert cap >= 128
+    big = _dims(num_seqs=64, max_seq_len=2048, max_blocks_per_seq=128, num_blocks=8192)
+    units = 64 * 8
+    assert ws(big) == (region(units * 4) + region((units + 256) * 4 * 64 * 4)
+                       + region((units + 256) * 4 * 2 * 4))
+    # twice as long: two windows per workgroup, so AUTO keeps the stream kernel
+    longer = _dims(num_seqs=64, max_seq_len=4096, max_blocks_per_seq=256, num_blocks=8192)
+    assert ws(longer) == ws(_dims(num_seqs=64, max_seq_len=4096, max_blocks_per_seq=256,
+                                  num_blocks=8192, kernel=3))
+    windows = -(-128 * 2 // cap)
+    assert ws(_dims(num_seqs=64, max_seq_len=4096, max_blocks_per_seq=256, num_blocks=8192,
+                    kernel=4)) == (region(units * 4)
+                                   + region((units + 256 * windows) * 4 * 64 * 4)
+                                   + region((units + 256 * windows) * 4 * 2 * 4))
+    assert ws(_dims(kernel=4, num_seqs=4096)) == BAD
+    assert ws(_dims(kernel=4, head_dim=80)) == BAD
+    assert ws(_dims(kernel=5)) == BAD
+
+
+def test_plan_kernel_reports_the_family():
+    plan = lambda d, bs=16: pkv.lib().pkv_decode_plan_kernel(ctypes.byref(d), bs)
+    assert plan(_dims()) == 4  # one window per workgroup holds the call
+    assert plan(_dims(num_seqs=64, max_seq_len=2048, max_blocks_per_seq=128)) == 4
+    # two windows per workgroup at 4096 tokens: the per-wavefront stream kernel
+    assert plan(_dims(num_seqs=64, max_seq_len=4096, max_blocks_per_seq=256)) == 3
+    assert plan(_dims(kernel=3)) == 3
+    assert plan(_dims(kernel=1)) == 1
+    assert plan(_dims(partition_size=32)) == 1  # a partition size asks for partitions
+    assert plan(_dims(num_seqs=4096)) == 1  # over the stream kernels' sequence limit
+    assert plan(_dims(head_dim=80)) == 2  # outside the matrix-core shapes
+    assert plan(_dims(kernel=4, head_dim=80)) == -1
+    assert plan(_dims(num_q_heads=30)) == -1
 
 
 def test_decode_rejects_before_any_hip_call():

@@ -74,7 +74,7 @@ CASES = {
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("kernel", ["stream", "mfma", "generic"])
+@pytest.mark.parametrize("kernel", ["stream_wg", "stream", "mfma", "generic"])
 def test_append_small(name, kernel):
     say(f"case append {name} kernel={kernel}")
     w = CASES[name]()
@@ -87,11 +87,12 @@ def test_append_small(name, kernel):
 
 
 @pytest.mark.parametrize("waves", [4, 64, 2048])
-def test_append_token_positions(waves):
+@pytest.mark.parametrize("kernel", ["stream", "stream_wg"])
+def test_append_token_positions(waves, kernel):
     """The new token at every position of a 32-token chunk and of a block:
     lengths 1..66 (block starts, block ends, chunk ends), and empty
     sequences, whose output is zero and whose cache is left alone."""
-    say(f"case append positions waves={waves}")
+    say(f"case append positions waves={waves} kernel={kernel}")
     lens = list(range(0, 67))
     w = workloads.random_small(65, len(lens), 8, 2, 64, 16, 66, min_len=0)
     r = workloads.rng(100, 79)
@@ -108,14 +109,15 @@ def test_append_token_positions(waves):
         bt[b, :nb] = perm[pos:pos + nb]
         pos += nb
     w.block_tables, w.num_blocks, w.poison_block = bt, pool, int(perm[-1])
-    out = _check(w, "stream", f"positions w{waves}", stream_waves=waves)
+    out = _check(w, kernel, f"positions w{waves}", stream_waves=waves)
     assert np.all(out[0].cpu().numpy() == 0)
 
 
-def test_two_steps():
+@pytest.mark.parametrize("kernel", ["stream", "stream_wg"])
+def test_two_steps(kernel):
     """Two decode steps back to back: the second appends position T_b (one
     past the first step's), which for some sequences opens a new block."""
-    say("case append two steps")
+    say(f"case append two steps kernel={kernel}")
     w = workloads.random_small(66, 8, 16, 4, 64, 16, 200, min_len=1, slack_blocks=20)
     # the tables need room for one more token: give every sequence a spare block
     spare = w.num_blocks
@@ -131,13 +133,13 @@ def test_two_steps():
     k2 = workloads.normal_bf16(r, (w.num_seqs, 4, 64))
     v2 = workloads.normal_bf16(r, (w.num_seqs, 4, 64))
     q2 = workloads.normal_bf16(r, (w.num_seqs, 16, 64))
-    kc, vc, out1 = _run(w, "stream")
+    kc, vc, out1 = _run(w, kernel)
     lens2 = w.seq_lens + 1
     out2 = torch.empty_like(out1)
     pkv.paged_attention_decode_append(
         bits_to_bf16(q2).to(DEV), bits_to_bf16(k2).to(DEV), bits_to_bf16(v2).to(DEV), kc, vc,
         torch.from_numpy(bt).to(DEV), torch.from_numpy(lens2.astype(np.int32)).to(DEV), 16,
-        w.scale, out2, max_seq_len=int(lens2.max()), kernel="stream")
+        w.scale, out2, max_seq_len=int(lens2.max()), kernel=kernel)
     # oracle: every token of both steps, sequence-major
     ks, vs = [], []
     cu = np.concatenate([[0], np.cumsum(w.seq_lens)])

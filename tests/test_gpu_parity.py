@@ -56,11 +56,11 @@ def matrix_core_shape(w) -> bool:
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("kernel", ["auto", "stream", "mfma", "generic"])
+@pytest.mark.parametrize("kernel", ["auto", "stream_wg", "stream", "mfma", "generic"])
 def test_decode_small(name, kernel):
     say(f"case decode {name} kernel={kernel}")
     w = SMALL[name]()
-    if kernel in ("stream", "mfma") and not matrix_core_shape(w):
+    if kernel in ("stream_wg", "stream", "mfma") and not matrix_core_shape(w):
         pytest.skip("shape outside the matrix-core kernels")
     g, o = GpuSide(w), OracleSide(w)
     ref = o.decode()
@@ -91,6 +91,50 @@ def test_stream_wave_counts(waves):
     compare(out.cpu().numpy(), ref, strict_abs=True, what=f"stream w{waves}")
 
 
+@pytest.mark.parametrize("waves", [8, 16, 72, 400, 2048])
+def test_stream_wg_group_counts(waves):
+    """Workgroups of 8 wavefronts: one group (the 9 sequences' ~2000 chunks
+    then need 14 windows in turn), two groups (7 windows each), 9, 50 and
+    256 groups (one window each, units cut into many pieces, more windows
+    than some units have chunks); lengths include 0 and 1."""
+    say(f"case stream_wg waves={waves}")
+    w = workloads.random_small(35, 9, 16, 4, 64, 16, 2100, min_len=0)
+    w.seq_lens[2] = 0
+    w.seq_lens[5] = 1
+    w.k_tok = w.k_tok[: int(w.seq_lens.sum())]
+    w.v_tok = w.v_tok[: int(w.seq_lens.sum())]
+    g, o = GpuSide(w), OracleSide(w)
+    ref = o.decode()
+    out = g.decode(torch.float32, kernel="stream_wg", stream_waves=waves)
+    assert np.all(out[2].cpu().numpy() == 0)
+    compare(out.cpu().numpy(), ref, strict_abs=True, what=f"stream_wg w{waves}")
+    outb = g.decode(torch.bfloat16, kernel="stream_wg", stream_waves=waves)
+    compare(outb.float().cpu().numpy(), ref, strict_abs=False, what=f"stream_wg w{waves} bf16")
+
+
+@pytest.mark.parametrize("name", ["g8_d128_b16", "g16_d64_b16", "g1_d64_b8", "g2_d64_b32"])
+def test_stream_wg_windows(name):
+    """One workgroup walking several windows at each head shape and block
+    size (head_dim 128: 4 wavefronts a group)."""
+    say(f"case stream_wg windows {name}")
+    w = SMALL[name]()
+    g, o = GpuSide(w), OracleSide(w)
+    ref = o.decode()
+    for waves in (4, 8):
+        out = g.decode(torch.float32, kernel="stream_wg", stream_waves=waves)
+        compare(out.cpu().numpy(), ref, strict_abs=True, what=f"{name} stream_wg w{waves}")
+
+
+def test_stream_wg_lengths_over_bound_give_nan():
+    """max_seq_len sizes the windows and the workspace; lengths far above it
+    (a broken contract) fill the output with NaN instead of overrunning LDS."""
+    say("case stream_wg over bound")
+    w = workloads.random_small(37, 4, 16, 4, 64, 16, 2000, min_len=1500)
+    g = GpuSide(w)
+    out = g.decode(torch.float32, kernel="stream_wg", stream_waves=8, max_seq_len=32)
+    assert torch.isnan(out).all()
+
+
 @pytest.mark.parametrize("num_seqs", [2048, 2100])
 def test_many_short_sequences(num_seqs):
     """The stream kernel keeps every length in LDS up to 2048 sequences;
@@ -101,6 +145,10 @@ def test_many_short_sequences(num_seqs):
     ref = o.decode()
     out = g.decode(torch.float32)
     compare(out.cpu().numpy(), ref, strict_abs=True, what=f"S{num_seqs} auto")
+    if num_seqs <= 2048:
+        for kernel in ("stream_wg", "stream"):
+            out = g.decode(torch.float32, kernel=kernel)
+            compare(out.cpu().numpy(), ref, strict_abs=True, what=f"S{num_seqs} {kernel}")
 
 
 @pytest.mark.parametrize("ps", [32, 64, 96, 256, 512, 1024])
@@ -153,23 +201,24 @@ def test_edge_lengths():
             out = g.decode(torch.float32, kernel=kernel, partition_size=ps).cpu().numpy()
             assert np.all(out[0] == 0)
             compare(out, ref, strict_abs=True, what=f"edges {kernel} ps{ps}")
-    for waves in (4, 16, 400):
-        out = g.decode(torch.float32, kernel="stream", stream_waves=waves).cpu().numpy()
-        assert np.all(out[0] == 0)
-        compare(out, ref, strict_abs=True, what=f"edges stream w{waves}")
+    for kernel in ("stream", "stream_wg"):
+        for waves in (4, 16, 400):
+            out = g.decode(torch.float32, kernel=kernel, stream_waves=waves).cpu().numpy()
+            assert np.all(out[0] == 0)
+            compare(out, ref, strict_abs=True, what=f"edges {kernel} w{waves}")
     # T = 1: the output is v_0 exactly (one weight of exactly 1)
     v0 = oracle.widen_bf16(w2.v_tok[0])  # sequence 1's only token (sequence 0 is empty)
-    for kernel in ("stream", "mfma", "generic"):
+    for kernel in ("stream_wg", "stream", "mfma", "generic"):
         out = g.decode(torch.float32, kernel=kernel).cpu().numpy()
         np.testing.assert_array_equal(out[1], np.repeat(v0, 4, axis=0))
 
 
-@pytest.mark.parametrize("kernel", ["stream", "mfma"])
+@pytest.mark.parametrize("kernel", ["stream_wg", "stream", "mfma"])
 def test_permutation_invariance_and_determinism(kernel):
     say(f"case permutation invariance {kernel}")
     w = workloads.random_small(33, 6, 16, 4, 64, 16, 700)
     g = GpuSide(w)
-    kw = dict(kernel=kernel, partition_size=0 if kernel == "stream" else 128)
+    kw = dict(kernel=kernel, partition_size=128 if kernel == "mfma" else 0)
     a = g.decode(torch.float32, **kw).cpu()
     b = g.decode(torch.float32, **kw).cpu()
     assert torch.equal(a, b), "repeated runs differ"

@@ -135,7 +135,7 @@ def test_prefix_sharing_copy_on_write():
     q = bits_to_bf16(w.q).to(DEV)
     btd = torch.from_numpy(bt).to(DEV)
     lens = torch.from_numpy(w.seq_lens).to(DEV)
-    for kernel, kw in (("stream", {}), ("mfma", dict(partition_size=256))):
+    for kernel, kw in (("stream_wg", {}), ("stream", {}), ("mfma", dict(partition_size=256))):
         for dt in (torch.float32, torch.bfloat16):
             out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=dt, device=DEV)
             pkv.paged_attention_decode(q, kc, vc, btd, lens, w.block_size, w.scale, out,
