@@ -13,11 +13,13 @@
 //         should synchronise little.
 //
 // Kernel families
-//   decode_stream   matrix-core kernel, the default.  The work of a call -
-//                   every (sequence, KV head) unit cut into 32-token chunks -
-//                   is dealt out in equal contiguous shares to a fixed set of
+//   decode_stream   matrix-core kernel.  The work of a call - every
+//                   (sequence, KV head) unit cut into 32-token chunks - is
+//                   dealt out in equal contiguous shares to a fixed set of
 //                   wavefronts, so all of them stream HBM until the end; a unit
-//                   cut between wavefronts is merged by the last of them.
+//                   cut between wavefronts is merged by the last of them.  (The
+//                   default, decode_wg in decode_wg.hip, deals the same work to
+//                   whole workgroups.)
 //   decode_mfma     matrix-core kernel over fixed partitions: one workgroup
 //                   per (partition, KV head, sequence), its waves taking the
 //                   partition's chunks round robin, split sequences merged by

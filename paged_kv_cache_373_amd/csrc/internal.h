@@ -24,8 +24,9 @@ struct DecodeParams {
   int32_t out_f32;            // 1: out is fp32, 0: out is bf16
   void* out;                  // [S, Hq, D]
   // Split-KV workspace.  Partitioned kernels (only when num_partitions > 1):
-  // partition results per (sequence, q head, partition).  Stream kernel: one
-  // slot of G heads per piece, [S * Hkv + waves] slots.
+  // partition results per (sequence, q head, partition).  Stream kernels: one
+  // slot of G heads per piece, [S * Hkv + waves] slots (per-wavefront ranges)
+  // or [S * Hkv + windows] slots (workgroup windows).
   float* part_out;            // [S, Hq, num_partitions, D] partition outputs
   float* part_lse;            // [S, Hq, num_partitions] ln Z_r (vector kernel)
   float* part_ml;             // [S, Hq, num_partitions, 2] (max in base-2 units, sum)
