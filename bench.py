@@ -15,6 +15,10 @@ total) that it cannot sit in the 256 MB Infinity Cache between steps.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
+``--workload`` is llama_b64 (default, the headline line) or long_splitkv;
+prefix_cow and pool16 print their own report lines instead (logical and
+unique GB/s with the copy_blocks time; the 16-layer pool step per block size).
+
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
 GPU.  ``roofline.achieved`` is the decode launch alone (HIP events on the
 stream it runs on); ``roofline.traffic`` is the HBM bytes per launch measured
@@ -106,6 +110,20 @@ def calibrate_copy(mib: int, reps: int) -> int:
     return 0
 
 
+def host_cpu() -> str:
+    """CPU model and logical CPU count of the host the oracle ran on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs"
+
+
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     """The oracle as it stands (fp64 C, OpenMP over (sequence, KV head)) on
     the host cores, over repetitions of the whole step until ~budget_s."""
@@ -119,10 +137,229 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
         t_total += time.perf_counter() - t0
         reps += 1
     per = t_total / reps
+    # the same on one thread, over a shorter budget
+    reps1, t1 = 0, 0.0
+    while t1 < budget_s / 3 and reps1 < 5000:
+        t0 = time.perf_counter()
+        oracle.dense_decode(w.q, w.k_tok, w.v_tok, w.seq_lens, w.scale, num_threads=1)
+        t1 += time.perf_counter() - t0
+        reps1 += 1
+    per1 = t1 / reps1
     return {"value": round(w.kv_bytes() / per / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"whole {w.name} step ({w.total_tokens} tokens x {w.num_kv_heads} KV heads)"
-                      f" repeated {reps}x, {per * 1e3:.1f} ms each, fp64 gather + dense attention"}
+                      f" repeated {reps}x, {per * 1e3:.1f} ms each, fp64 gather + dense attention",
+            "single_thread": {"value": round(w.kv_bytes() / per1 / 1e9, 3), "unit": "GB/s",
+                              "sample": f"{reps1}x, {per1 * 1e3:.1f} ms each"},
+            "host": host_cpu()}
+
+
+def read_ceiling(pkv, torch, dev, stream, kv_bytes: int, launches: int) -> dict:
+    """Context for the roofline: the library's trivial read kernel over the
+    step's byte count as whole 2 KiB tiles in random order (the cache's access
+    pattern), rotating over 8 regions so that none is cache resident."""
+    tiles = (kv_bytes // 2048) // 32 * 32
+    regions = 8
+    src = torch.zeros(regions * tiles * 2048, dtype=torch.uint8, device=dev)
+    g = torch.Generator().manual_seed(373)
+    orders = [(torch.randperm(tiles, generator=g) + r * tiles).to(torch.int32).to(dev)
+              for r in range(regions)]
+    sink = torch.empty(tiles * 8, dtype=torch.int32, device=dev)
+    for r in range(2 * regions):
+        pkv.read_probe(src, orders[r % regions], sink)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(launches):
+        pkv.read_probe(src, orders[r % regions], sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    gbs = tiles * 2048 / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 2), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "us_per_launch": round(ms * 1e3, 3), "bytes": tiles * 2048,
+            "kind": "trivial read kernel (pkv_read_probe): the step's byte count as 2 KiB "
+                    "tiles in random order, 8 rotated regions, launches back to back"}
+
+
+def timed(stream, fn, launches: int, warmup: int = 3) -> float:
+    """Milliseconds per call of fn(i), `launches` calls back to back between
+    one pair of events on `stream` (after `warmup` untimed calls)."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(launches):
+        fn(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / launches
+
+
+def run_prefix_cow(args) -> int:
+    """The shared-prefix workload: 4 prompts x 1000 tokens forked 16 ways
+    (B = 16), 1..300 private tokens per fork, the shared 8-token tails copied
+    with copy_blocks before the first private write.  Reports the decode on
+    logical bytes (every fork's tokens) and on unique bytes (each physical
+    block once), and the copy_blocks launch on its own."""
+    import torch
+
+    import paged_kv_cache_373_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    w = workloads.prefix_sharing()
+    ex = w.extra
+    P, L, F, bs = ex["num_prompts"], ex["prompt_len"], ex["forks"], w.block_size
+    hkv, d = w.num_kv_heads, w.head_dim
+    bm = pkv.BlockManager(w.num_blocks, bs, free_order=w.free_list)
+    cu = w.cu_seqlens
+    prompt_slots, private = [], []
+    for p in range(P):
+        bm.add_sequence(("prompt", p))
+        prompt_slots.append(bm.append_tokens(("prompt", p), L)[0])
+    for p in range(P):
+        for f in range(F):
+            bm.fork(("prompt", p), p * F + f)
+        bm.release(("prompt", p))
+    pairs = []
+    for b in range(w.num_seqs):
+        slots, copies = bm.append_tokens(b, int(ex["n_private"][b]))
+        pairs += copies
+        private.append((slots, cu[b] + L + np.arange(int(ex["n_private"][b]))))
+    bt = torch.from_numpy(bm.block_table_array(list(range(w.num_seqs)), pad=0)).to(dev)
+    used = sorted({blk for b in range(w.num_seqs) for blk in bm.table(b)})
+    # unique bytes: each physical block's valid tokens once
+    valid = {}
+    for b in range(w.num_seqs):
+        T = int(w.seq_lens[b])
+        for j, blk in enumerate(bm.table(b)):
+            valid[blk] = max(valid.get(blk, 0), min(bs, T - j * bs))
+    unique_tokens = sum(valid.values())
+    pool_bytes = 2 * w.num_blocks * hkv * bs * d * 2
+    copies = args.copies or max(2, math.ceil(ROTATE_BYTES / pool_bytes))
+    kt, vt = bits_to_bf16(w.k_tok).to(dev), bits_to_bf16(w.v_tok).to(dev)
+    pairs_d = torch.tensor(pairs, dtype=torch.int32, device=dev)
+    caches = []
+    for _ in range(copies):
+        kc, vc = pkv.new_kv_cache(w.num_blocks, hkv, bs, d, device=dev, fill=float("nan"))
+        for p in range(P):
+            rows = torch.from_numpy(cu[p * F] + np.arange(L)).to(dev)
+            pkv.reshape_and_cache(kt[rows], vt[rows], torch.from_numpy(prompt_slots[p]).to(dev),
+                                  kc, vc)
+        pkv.copy_blocks([kc], [vc], pairs_d)
+        for slots, rows in private:
+            r = torch.from_numpy(rows).to(dev)
+            pkv.reshape_and_cache(kt[r], vt[r], torch.from_numpy(slots).to(dev), kc, vc)
+        caches.append((kc, vc))
+    q = bits_to_bf16(w.q).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    out = torch.empty((w.num_seqs, w.num_q_heads, d), dtype=torch.bfloat16, device=dev)
+    ws = pkv.DecodeWorkspace(device=dev)
+    kw = dict(max_seq_len=int(w.seq_lens.max()), kernel=args.kernel, workspace=ws)
+
+    def dec(i):
+        kc, vc = caches[i % copies]
+        pkv.paged_attention_decode(q, kc, vc, bt, lens, bs, w.scale, out, **kw)
+
+    def cow(i):
+        kc, vc = caches[i % copies]
+        pkv.copy_blocks([kc], [vc], pairs_d)
+
+    ms = timed(stream, dec, args.steps, args.warmup)
+    ms_cow = timed(stream, cow, args.steps, args.warmup)
+    logical = w.kv_bytes()
+    unique = unique_tokens * hkv * d * 2 * 2
+    print(json.dumps({
+        "workload": "prefix_cow", "kernel": pkv.decode_plan_kernel(q, caches[0][0], bt,
+                                                                    max_seq_len=kw["max_seq_len"],
+                                                                    kernel=args.kernel),
+        "decode_us": round(ms * 1e3, 3),
+        "logical_kv_bytes": logical, "logical_gbs": round(logical / (ms * 1e-3) / 1e9, 1),
+        "unique_kv_bytes": unique, "unique_gbs": round(unique / (ms * 1e-3) / 1e9, 1),
+        "copy_blocks_pairs": len(pairs), "copy_blocks_bytes": 2 * len(pairs) * hkv * bs * d * 2,
+        "copy_blocks_us": round(ms_cow * 1e3, 3), "cache_copies_rotated": copies,
+        "blocks_in_use": len(used), "steps": args.steps}), flush=True)
+    return 0
+
+
+def run_pool16(args) -> int:
+    """The 16-layer decode step at pool scale: 2^22 slots per layer (8 GiB of
+    K+V per layer), 256 sequences with lognormal lengths (median 1200, capped
+    at 8192), B in {8, 16, 32}.  One step = the 16 layers' decode launches in
+    turn; with the writer each launch also stores its layer's new token
+    (paged_attention_decode_append), without it only attends.  K/V values are
+    drawn on the device (the timing does not depend on them)."""
+    import torch
+
+    import paged_kv_cache_373_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    res = {"workload": "pool16", "layers": workloads.POOL_LAYERS, "by_block_size": {}}
+    for bs in (8, 16, 32):
+        w = workloads.pool_step(bs)
+        S, hq, hkv, d = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+        bm = pkv.BlockManager(w.num_blocks, bs, free_order=w.free_list)
+        slot_list = []
+        for b in range(S):
+            bm.add_sequence(b)
+            slot_list.append(bm.append_tokens(b, int(w.seq_lens[b]))[0])
+        slots = np.concatenate(slot_list)
+        cu = w.cu_seqlens
+        last = cu[1:] - 1
+        pre = slots.copy()
+        pre[last] = -1
+        bt = torch.from_numpy(bm.block_table_array(list(range(S)), pad=0)).to(dev)
+        lens = torch.from_numpy(w.seq_lens).to(dev)
+        kt, vt = workloads.pool_layer_tokens_device(0, int(cu[-1]), dev, bs)
+        pre_d = torch.from_numpy(pre).to(dev)
+        lastd = torch.from_numpy(last).to(dev)
+        layers = []
+        for layer in range(workloads.POOL_LAYERS):
+            kc, vc = pkv.new_kv_cache(w.num_blocks, hkv, bs, d, device=dev)
+            pkv.reshape_and_cache(kt, vt, pre_d, kc, vc)
+            q = bits_to_bf16(workloads.pool_layer_q(layer, S)).to(dev)
+            layers.append((kc, vc, q))
+        k_new, v_new = kt[lastd].contiguous(), vt[lastd].contiguous()
+        del kt, vt
+        out = torch.empty((S, hq, d), dtype=torch.bfloat16, device=dev)
+        ws = pkv.DecodeWorkspace(device=dev)
+        kw = dict(max_seq_len=int(w.seq_lens.max()), kernel=args.kernel, workspace=ws)
+
+        def step_append(i):
+            for kc, vc, q in layers:
+                pkv.paged_attention_decode_append(q, k_new, v_new, kc, vc, bt, lens, bs, w.scale,
+                                                  out, **kw)
+
+        def step_decode(i):
+            for kc, vc, q in layers:
+                pkv.paged_attention_decode(q, kc, vc, bt, lens, bs, w.scale, out, **kw)
+
+        n = max(args.steps // 10, 5)
+        ms_a = timed(stream, step_append, n, 2)
+        ms_d = timed(stream, step_decode, n, 2)
+        per_layer = w.kv_bytes()
+        res["by_block_size"][str(bs)] = {
+            "kernel": pkv.decode_plan_kernel(layers[0][2], layers[0][0], bt,
+                                             max_seq_len=kw["max_seq_len"], kernel=args.kernel),
+            "tokens_per_layer": w.total_tokens, "kv_bytes_per_layer": per_layer,
+            "step_ms_with_writer": round(ms_a, 4), "step_ms_without_writer": round(ms_d, 4),
+            "per_layer_gbs_with_writer": round(16 * per_layer / (ms_a * 1e-3) / 1e9, 1),
+            "per_layer_gbs_without_writer": round(16 * per_layer / (ms_d * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(S / (ms_a * 1e-3), 1), "steps": n}
+        log(f"pool16 B={bs}: step {ms_a:.3f} ms with the writer, {ms_d:.3f} ms without")
+        del layers, out
+        torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -132,6 +369,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama_b64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trials", type=int, default=5,
+                    help="timed regions of --steps steps each; value is their median")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the trivial read kernel timed over the step's byte count")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: >1 GiB)")
@@ -152,6 +393,10 @@ def main() -> int:
 
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, max(args.steps, 1))
+    if args.workload == "prefix_cow":
+        return run_prefix_cow(args)
+    if args.workload == "pool16":
+        return run_pool16(args)
 
     import torch
 
@@ -222,29 +467,35 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
-    # The timed region: K steps back to back between one pair of events on the
-    # stream the kernels run on.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    # Each timed region: K steps back to back between one pair of events on
+    # the stream the kernels run on, synchronised on both sides.  The value is
+    # the median over the trials.
+    trial_ms = []
+    nxt = args.warmup
+    for _ in range(max(args.trials, 1)):
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(nxt + i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        nxt += args.steps
+        trial_ms.append(t_start.elapsed_time(t_end) / args.steps)
+    ms_step = float(np.median(trial_ms))
     if args.unfused:
         # the decode launch on its own: one event pair around each launch
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for i in range(args.steps):
-            step(args.warmup + args.steps + i, evs[i])
+            step(nxt + i, evs[i])
         torch.cuda.synchronize()
         decode_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     else:
         decode_ms = ms_step  # the step is the one launch
-    log(f"step {ms_step * 1e3:.2f} us, decode launch {decode_ms * 1e3:.2f} us")
+    log(f"step {ms_step * 1e3:.2f} us (median of {len(trial_ms)} trials: "
+        f"{', '.join(f'{t * 1e3:.2f}' for t in trial_ms)}), decode launch {decode_ms * 1e3:.2f} us")
 
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (decode_ms * 1e-3) / 1e9
@@ -283,6 +534,14 @@ def main() -> int:
             "avg_launch_us": round(decode_ms * 1e3, 3),
         },
     }
+    result["trials"] = {"ms_per_step": [round(t, 5) for t in trial_ms],
+                        "median": round(ms_step, 5), "min": round(min(trial_ms), 5),
+                        "max": round(max(trial_ms), 5)}
+    if not args.no_read_ceiling:
+        del caches
+        torch.cuda.empty_cache()
+        result["read_ceiling"] = read_ceiling(pkv, torch, dev, stream, kv_bytes, args.steps)
+        log(f"read ceiling {result['read_ceiling']['value']} GB/s")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(w)

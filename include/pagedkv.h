@@ -270,6 +270,17 @@ const char* pkv_status_string(int32_t status);
 /* Version of this ABI: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
 
+/* Measurement helper, not part of the attention path: reads num_tiles tiles
+ * of 2048 bytes from `src` (device, 16-byte aligned), tile order[i] being the
+ * i-th read (order: device int32 [num_tiles], each in range), and writes one
+ * folded word per thread to `sink` (device, num_tiles * 8 uint32).  num_tiles
+ * must be a positive multiple of 32.  The benchmark times it over the decode
+ * step's byte count as the streaming-read ceiling of the cache's access
+ * pattern (whole 2 KiB (block, head) tiles in random order).
+ * Returns PKV_OK, or an error status with nothing enqueued. */
+pkv_status pkv_read_probe(const void* src, const int32_t* order, int64_t num_tiles,
+                          uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

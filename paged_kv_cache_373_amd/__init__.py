@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_copy_blocks.restype = ctypes.c_int
         L.pkv_merge_attention_states.argtypes = [vp, vp, i32, i32, i32, vp, ctypes.c_int, vp]
         L.pkv_merge_attention_states.restype = ctypes.c_int
+        L.pkv_read_probe.argtypes = [vp, vp, i64, vp, vp]
+        L.pkv_read_probe.restype = ctypes.c_int
         L.pkv_status_string.argtypes = [i32]
         L.pkv_status_string.restype = ctypes.c_char_p
         L.pkv_abi_version.restype = i32
@@ -385,3 +387,20 @@ def merge_attention_states(part_out: torch.Tensor, part_lse: torch.Tensor,
     if st != PKV_OK:
         raise PagedKVError(st, "pkv_merge_attention_states")
     return out
+
+
+def read_probe(src: torch.Tensor, order: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper: read ``order.numel()`` 2 KiB tiles of ``src`` (a
+    uint8 device tensor) in the given order; ``sink`` (int32, numel >= 8 x
+    tiles) receives one folded word per thread.  Not part of the attention
+    path: the benchmark's streaming-read ceiling."""
+    _check(src, "src", torch.uint8, 1)
+    _check(order, "order", torch.int32, 1)
+    _check(sink, "sink", torch.int32, 1)
+    n = order.numel()
+    if n % 32 != 0 or sink.numel() < 8 * n:
+        raise ValueError("order must hold a multiple of 32 tiles and sink 8 words per tile")
+    st = lib().pkv_read_probe(src.data_ptr(), order.data_ptr(), n, sink.data_ptr(),
+                              _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_read_probe")

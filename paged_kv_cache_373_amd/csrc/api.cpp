@@ -383,6 +383,15 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
                                             static_cast<hipStream_t>(stream)));
 }
 
+pkv_status pkv_read_probe(const void* src, const int32_t* order, int64_t num_tiles,
+                          uint32_t* sink, void* stream) {
+  if (num_tiles <= 0 || num_tiles % 32 != 0 || num_tiles / 32 > 0x7FFFFFFF) return PKV_ERR_INVALID;
+  if (src == nullptr || order == nullptr || sink == nullptr || !aligned16(src))
+    return PKV_ERR_INVALID;
+  return hip_status(
+      pkv::launch_read_probe(src, order, num_tiles, sink, static_cast<hipStream_t>(stream)));
+}
+
 pkv_status pkv_merge_attention_states(const float* part_out, const float* part_lse,
                                       int32_t num_rows, int32_t num_parts, int32_t head_dim,
                                       void* out, pkv_dtype out_dtype, void* stream) {

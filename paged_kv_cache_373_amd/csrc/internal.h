@@ -100,6 +100,11 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v,
                                     int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache,
                                     uint16_t* v_cache, int32_t block_size, hipStream_t stream);
 
+// Measurement helper: reads num_tiles 2 KiB tiles of src in the order given
+// (num_tiles a multiple of 32; sink holds num_tiles * 8 words).
+hipError_t launch_read_probe(const void* src, const int32_t* order, int64_t num_tiles,
+                             uint32_t* sink, hipStream_t stream);
+
 constexpr int kMaxCopyLayers = 64;
 hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                               const int32_t* block_pairs, int32_t num_pairs,

@@ -217,6 +217,17 @@ def test_append_rejects_before_any_hip_call():
     assert call(f, f, _dims(num_q_heads=30)) == pkv.PKV_ERR_INVALID
 
 
+def test_read_probe_rejects_before_any_hip_call():
+    lib = pkv.lib()
+    f = ctypes.c_void_p(0x1000)
+    lib.pkv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.pkv_read_probe(f, f, 0, f, None) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_read_probe(f, f, 48, f, None) == pkv.PKV_ERR_INVALID  # not a multiple of 32
+    assert lib.pkv_read_probe(None, f, 32, f, None) == pkv.PKV_ERR_INVALID
+    assert lib.pkv_read_probe(ctypes.c_void_p(0x1008), f, 32, f, None) == pkv.PKV_ERR_INVALID
+
+
 def test_writers_reject_before_any_hip_call():
     lib = pkv.lib()
     f = ctypes.c_void_p(0x1000)

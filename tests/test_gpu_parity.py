@@ -318,3 +318,26 @@ def test_workspace_reuse_across_shapes():
                          False)
         z = pkv.lib().pkv_decode_workspace_zeroed_bytes(pkv.ctypes.byref(dims), w.block_size)
         assert int(raw[:z].count_nonzero()) == 0
+
+
+def test_read_probe_folds_every_tile():
+    """The measurement helper reads each tile it is given: thread t of
+    workgroup g folds 16 bytes of each of its 16 tiles (XOR of 4 words)."""
+    say("case read probe")
+    r = np.random.default_rng(9)
+    tiles = 64
+    src = r.integers(0, 2**32, size=(tiles * 2048) // 4, dtype=np.uint32)
+    order = r.permutation(tiles).astype(np.int32)
+    sink = torch.zeros(tiles * 8, dtype=torch.int32, device=DEV)
+    pkv.read_probe(torch.from_numpy(src.view(np.uint8)).to(DEV), torch.from_numpy(order).to(DEV),
+                   sink)
+    words = src.reshape(tiles, 128, 4)  # tile, 16-byte piece, word
+    exp = np.zeros((tiles // 32, 256), dtype=np.uint32)
+    for g in range(tiles // 32):
+        for t in range(256):
+            half, l = divmod(t, 128)
+            x = 0
+            for j in range(16):
+                x ^= int(np.bitwise_xor.reduce(words[order[32 * g + 2 * j + half], l]))
+            exp[g, t] = x
+    np.testing.assert_array_equal(sink.cpu().numpy().view(np.uint32).reshape(-1, 256), exp)
