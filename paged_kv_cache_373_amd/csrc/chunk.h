@@ -170,11 +170,18 @@ struct Mfma {
   // element offsets `base` (wave-uniform).
   static __device__ void load(const uint16_t* k_cache, const uint16_t* v_cache,
                               const size_t (&base)[NB], const Lane& ln, Regs& x) {
+    // base[j] for this lane's block j (a lane constant): two levels of
+    // selects on the bits of j, so the choice stays in registers
     auto pick = [&](int j) {
-      size_t v = base[0];
-#pragma unroll
-      for (int jj = 1; jj < NB; ++jj) v = (j == jj) ? base[jj] : v;
-      return v;
+      if constexpr (NB == 1) {
+        return base[0];
+      } else if constexpr (NB == 2) {
+        return (j == 1) ? base[1] : base[0];
+      } else {
+        const size_t lo = (j & 1) ? base[1] : base[0];
+        const size_t hi = (j & 1) ? base[3] : base[2];
+        return (j & 2) ? hi : lo;
+      }
     };
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
