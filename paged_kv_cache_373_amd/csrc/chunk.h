@@ -256,38 +256,62 @@ struct Mfma {
 };
 
 
+// The new token of a fused decode step: its K and V rows (bf16 [D] each) in
+// the layout the patch below needs - lane (c, r) holds dims [32 hs + 8 c, +8)
+// of K for each hs, and feature 16 nt + r of V for each nt.  Loaded together
+// with a chunk, through buffer resources whose size is the row's for the
+// chunk holding a unit's last position and 0 for every other chunk: the
+// loads are issued for every chunk, which keeps the ring's wait counts exact,
+// but only the needed ones touch memory (a size-0 resource reads nothing and
+// returns zeros).
+template <int D>
+struct NewToken {
+  static constexpr int HS = D / 32;
+  static constexpr int NT = D / 16;
+  bf16x8_t k[HS];
+  uint16_t v[NT];
+  __device__ void load(const uint16_t* k_row, const uint16_t* v_row, bool needed, int c, int r) {
+    constexpr int kRsrcWord3 = 0x00020000;
+    const int bytes = needed ? D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k_row), 0, bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v_row), 0, bytes, kRsrcWord3);
+#pragma unroll
+    for (int hs = 0; hs < HS; ++hs)
+      k[hs] = __builtin_bit_cast(bf16x8_t,
+                                 __builtin_amdgcn_raw_buffer_load_b128(rk, (32 * hs + 8 * c) * 2, 0, 0));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      v[nt] = __builtin_amdgcn_raw_buffer_load_b16(rv, (16 * nt + r) * 2, 0, 0);
+  }
+};
+
 // The new token of a fused decode step sits at position tn = valid - 1 of its
-// unit's last chunk.  Its K and V rows (from k_new / v_new) replace that
-// position's operands in `x` - the cache slot has been read but not yet
+// unit's last chunk.  Its K and V rows (`nt`, loaded with the chunk) replace
+// that position's operands in `x` - the cache slot has been read but not yet
 // written - and are stored to the slot: block `blk` of the chunk (the one
 // holding position tn), offset tn % BS.  Lane roles as in Mfma.
 template <int D, int BS>
 __device__ __forceinline__ void patch_new_token(const DecodeParams& prm,
-                                                typename Mfma<D, BS>::Regs& x, int valid, int b,
-                                                int hh, int blk, int lane) {
+                                                typename Mfma<D, BS>::Regs& x,
+                                                const NewToken<D>& nt, int valid, int hh,
+                                                int blk, int lane) {
   using M = Mfma<D, BS>;
   constexpr int HS = M::HS;
   constexpr int NT = M::NT;
   const int c = lane >> 4;
   const int r = lane & 15;
   const int tn = valid - 1;
-  const size_t src = (static_cast<size_t>(b) * prm.num_kv_heads + hh) * D;
   const int un = (tn & 7) >> 2;             // K operand half holding the token
   const int rn = 4 * (tn >> 3) + (tn & 3);  // and its lane row
   const int cn = tn >> 3;                   // V operand lane group holding the token
   const int en = tn & 7;                    // and its element
-  bf16x8_t kn[HS];
-#pragma unroll
-  for (int hs = 0; hs < HS; ++hs) kn[hs] = load_bf16x8(prm.k_new + src + 32 * hs + 8 * c);
-  uint16_t vn[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) vn[nt] = prm.v_new[src + 16 * nt + r];
-  __builtin_amdgcn_s_waitcnt(0);
   const bool in0 = (r == rn) && (un == 0);
   const bool in1 = (r == rn) && (un == 1);
 #pragma unroll
   for (int hs = 0; hs < HS; ++hs) {
-    const u32x4_t nk = __builtin_bit_cast(u32x4_t, kn[hs]);
+    const u32x4_t nk = __builtin_bit_cast(u32x4_t, nt.k[hs]);
     const u32x4_t o0 = __builtin_bit_cast(u32x4_t, x.k[0][hs]);
     const u32x4_t o1 = __builtin_bit_cast(u32x4_t, x.k[1][hs]);
     u32x4_t r0, r1;
@@ -301,20 +325,24 @@ __device__ __forceinline__ void patch_new_token(const DecodeParams& prm,
   }
   if (c == cn) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        x.v[nt][e] = (e == en) ? __builtin_bit_cast(__bf16, vn[nt]) : x.v[nt][e];
+        x.v[n][e] = (e == en) ? __builtin_bit_cast(__bf16, nt.v[n]) : x.v[n][e];
   }
   const size_t tile = (static_cast<size_t>(blk) * prm.num_kv_heads + hh) * M::kTile;
   const int off = tn % BS;
-  if (lane < 4 * HS) {  // K row: HS x 4 pieces of 16 bytes
-    const int hs = lane >> 2, cc4 = lane & 3;
-    *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 32 * hs + 8 * cc4) =
-        *reinterpret_cast<const u32x4_t*>(prm.k_new + src + 32 * hs + 8 * cc4);
+  if (r == 0) {  // lanes (c, 0): dims [32 hs + 8 c, +8) of the K row
+#pragma unroll
+    for (int hs = 0; hs < HS; ++hs)
+      *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 32 * hs + 8 * c) =
+          __builtin_bit_cast(u32x4_t, nt.k[hs]);
   }
-  for (int d = lane; d < D; d += 64)
-    prm.v_cache_w[tile + static_cast<size_t>(d) * BS + off] = prm.v_new[src + d];
+  if (c == 0) {  // lanes (0, r): features 16 nt + r of the V row
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      prm.v_cache_w[tile + static_cast<size_t>(16 * n + r) * BS + off] = nt.v[n];
+  }
 }
 
 // Sequence lengths into s_len[0, S) and the exclusive prefix of per-sequence

@@ -135,6 +135,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
   struct Slot {  // one ring entry: a chunk's K/V operands and its unit's query group
     Regs x;
     bf16x8_t q[HS];
+    NewToken<D> nt;  // the new token of a fused decode step (zeros where none)
   };
   int pb = 0, ph = 0, plc0 = 0;  // the piece being folded: sequence, KV head, first chunk
 
@@ -359,6 +360,10 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       // the chunk's query group travels with it (512 bytes per unit, cached
       // after its first chunk), so a piece starting needs no load of its own
       M::load_q(q, Hq, G, __builtin_amdgcn_readlane(cb, i), hh, c, r, sl8.q);
+      const bool fresh = prm.k_new != nullptr && (__builtin_amdgcn_readlane(cfl, i) & 4) != 0;
+      const size_t row = (static_cast<size_t>(__builtin_amdgcn_readlane(cb, i)) * Hkv + hh) * D;
+      sl8.nt.load(fresh ? prm.k_new + row : nullptr, fresh ? prm.v_new + row : nullptr, fresh, c,
+                  r);
     };
     auto consume = [&](int i, Slot& sl8) {
       Regs& x = sl8.x;
@@ -372,7 +377,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       const int valid = __builtin_amdgcn_readlane(cval, i);
       if ((fl & 4) && prm.k_new != nullptr) {
         // The unit's last chunk holds the new token (chunk position
-        // valid - 1): its K/V come from k_new/v_new into the operand registers
+        // valid - 1): its K/V, loaded with the chunk, replace the operands
         // (the cache slot was read before it is written), then go to the slot.
         const int tn = valid - 1;
         // the chunk's block holding position tn
@@ -380,8 +385,8 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
 #pragma unroll
         for (int j = 1; j < NB; ++j)
           blk = (tn / BS == j) ? __builtin_amdgcn_readlane(ent[j], i) : blk;
-        patch_new_token<D, BS>(prm, x, valid, __builtin_amdgcn_readlane(cb, i),
-                               __builtin_amdgcn_readlane(chd, i), blk, lane);
+        patch_new_token<D, BS>(prm, x, sl8.nt, valid, __builtin_amdgcn_readlane(chd, i), blk,
+                               lane);
       }
       M::step(sl8.q, x, valid, sl, c, st);
       if (fl & 2) finish_piece(__builtin_amdgcn_readlane(clc, i));

@@ -308,10 +308,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       const int vf = __builtin_amdgcn_readfirstlane(rec[3]);
       const int valid = vf & 255;
       if (((vf >> 8) & 4) && prm.k_new != nullptr) {
-        // the unit's last chunk holds the new token of a fused decode step
+        // The unit's last chunk holds the new token of a fused decode step.
+        // Its rows are loaded here, which makes this wavefront wait for its
+        // other chunk in flight too; the other wavefronts take up the slack.
         const int tn = valid - 1;
-        patch_new_token<D, BS>(prm, sl8.x, valid, __builtin_amdgcn_readfirstlane(rec[0]),
-                               __builtin_amdgcn_readfirstlane(rec[1]),
+        const int hh = __builtin_amdgcn_readfirstlane(rec[1]);
+        const size_t row =
+            (static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[0])) * Hkv + hh) * D;
+        NewToken<D> nt;
+        nt.load(prm.k_new + row, prm.v_new + row, true, c, r);
+        __builtin_amdgcn_s_waitcnt(0);
+        patch_new_token<D, BS>(prm, sl8.x, nt, valid, hh,
                                __builtin_amdgcn_readfirstlane(rec[kRecBase + tn / BS]), lane);
       }
       typename M::State st;
