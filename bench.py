@@ -204,9 +204,10 @@ def timed(stream, fn, launches: int, warmup: int = 3) -> float:
 def run_prefix_cow(args) -> int:
     """The shared-prefix workload: 4 prompts x 1000 tokens forked 16 ways
     (B = 16), 1..300 private tokens per fork, the shared 8-token tails copied
-    with copy_blocks before the first private write.  Reports the decode on
-    logical bytes (every fork's tokens) and on unique bytes (each physical
-    block once), and the copy_blocks launch on its own."""
+    with copy_blocks before the first private write.  Reports the decode and
+    the shared-prefix (cascade) decode on logical bytes (every fork's tokens)
+    and on unique bytes (each physical block once), and the copy_blocks
+    launch on its own."""
     import torch
 
     import paged_kv_cache_373_amd as pkv
@@ -272,7 +273,21 @@ def run_prefix_cow(args) -> int:
         kc, vc = caches[i % copies]
         pkv.copy_blocks([kc], [vc], pairs_d)
 
+    gs_np, pl_np = bm.shared_prefix_groups(list(range(w.num_seqs)))
+    gs, pl = torch.from_numpy(gs_np).to(dev), torch.from_numpy(pl_np).to(dev)
+    cws = torch.empty(pkv.cascade_workspace_size(q, caches[0][0], bt, len(pl_np),
+                                                 int(pl_np.max()),
+                                                 max_seq_len=kw["max_seq_len"]),
+                      dtype=torch.uint8, device=dev)
+
+    def casc(i):
+        kc, vc = caches[i % copies]
+        pkv.cascade_decode(q, kc, vc, bt, lens, gs, pl, bs, w.scale, out,
+                           max_prefix_len=int(pl_np.max()), max_seq_len=kw["max_seq_len"],
+                           workspace=cws)
+
     ms = timed(stream, dec, args.steps, args.warmup)
+    ms_casc = timed(stream, casc, args.steps, args.warmup)
     ms_cow = timed(stream, cow, args.steps, args.warmup)
     logical = w.kv_bytes()
     unique = unique_tokens * hkv * d * 2 * 2
@@ -283,6 +298,10 @@ def run_prefix_cow(args) -> int:
         "decode_us": round(ms * 1e3, 3),
         "logical_kv_bytes": logical, "logical_gbs": round(logical / (ms * 1e-3) / 1e9, 1),
         "unique_kv_bytes": unique, "unique_gbs": round(unique / (ms * 1e-3) / 1e9, 1),
+        "cascade_us": round(ms_casc * 1e3, 3),
+        "cascade_logical_gbs": round(logical / (ms_casc * 1e-3) / 1e9, 1),
+        "cascade_unique_gbs": round(unique / (ms_casc * 1e-3) / 1e9, 1),
+        "cascade_groups": int(len(pl_np)), "cascade_prefix_tokens": int(pl_np.max()),
         "copy_blocks_pairs": len(pairs), "copy_blocks_bytes": 2 * len(pairs) * hkv * bs * d * 2,
         "copy_blocks_us": round(ms_cow * 1e3, 3), "cache_copies_rotated": copies,
         "blocks_in_use": len(used), "steps": args.steps}), flush=True)

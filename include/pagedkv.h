@@ -264,6 +264,51 @@ pkv_status pkv_merge_attention_states(const float* part_out, const float* part_l
                                       int32_t head_dim, void* out,
                                       pkv_dtype out_dtype, void* stream);
 
+/* Shared-prefix ("cascade") decode [PU §共享前缀，分叉时 Copy-on-write: the
+ * samples of one prompt point their block tables at the same physical blocks
+ * for the prompt, and full prefix blocks stay shared; PU §按 Block 分配:
+ * per-segment results merge by o = (Z1 o1 + Z2 o2) / (Z1 + Z2) after
+ * rescaling to a common maximum, segments need not follow physical blocks].
+ * Computes exactly what pkv_paged_attention_decode computes for the same q,
+ * caches, tables and lengths, but reads the blocks a group shares once for
+ * the whole group: each sequence's tokens are cut into its group's shared
+ * prefix and its own suffix, the prefix is attended by all members' queries
+ * together, and the two segment results are merged.
+ *
+ *   group_starts  device int32 [num_groups + 1]: group g is the sequences
+ *                 [group_starts[g], group_starts[g+1]); group_starts[0] = 0,
+ *                 strictly increasing, group_starts[num_groups] = S.  A
+ *                 sequence that shares nothing is a group of one.
+ *   prefix_lens   device int32 [num_groups]: L_g, the tokens every member of
+ *                 group g shares; a multiple of block_size, 0 <= L_g <=
+ *                 max_prefix_len, L_g <= T_b for every member b, and the first
+ *                 L_g / block_size entries of every member's table row are the
+ *                 same physical blocks (the first member's row is read).
+ *   num_groups    1 <= num_groups <= S (when S > 0).
+ *   max_prefix_len  host bound on every L_g, <= dims->max_seq_len.
+ *   dims          as for pkv_paged_attention_decode; `kernel`,
+ *                 `partition_size`, `waves_per_group`, `balance_partitions` and
+ *                 `stream_waves` are ignored.  head_dim 64 or 128, block_size
+ *                 8, 16 or 32, group <= 16, S <= 4096 (PKV_ERR_UNSUPPORTED
+ *                 otherwise).
+ *   workspace     device scratch of at least pkv_cascade_workspace_size bytes,
+ *                 256-byte aligned; needs no initialisation and holds garbage
+ *                 after the call.
+ * If a device-side condition above fails (groups not a partition of the
+ * sequences, L_g not a multiple of block_size or above max_prefix_len, a
+ * member shorter than L_g, some T_b above dims->max_seq_len), every output row
+ * is NaN.  Two launches on `stream`: the segments' partial states, then their
+ * merge.  q, k_cache and v_cache 16-byte aligned.
+ * Returns PKV_OK, or an error status with nothing enqueued. */
+size_t pkv_cascade_workspace_size(const pkv_decode_dims* dims, int32_t num_groups,
+                                  int32_t max_prefix_len, int32_t block_size);
+pkv_status pkv_cascade_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* group_starts, const int32_t* prefix_lens,
+                              int32_t num_groups, int32_t max_prefix_len, int32_t block_size,
+                              float scale, void* out, const pkv_decode_dims* dims,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int32_t status);
 

@@ -21,7 +21,7 @@ from .block_manager import BlockManager, PoolExhaustedError, slot_mapping_for
 
 __all__ = [
     "lib", "paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
-    "copy_blocks",
+    "copy_blocks", "cascade_decode", "cascade_workspace_size",
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
     "BlockManager",
     "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
@@ -91,6 +91,11 @@ def lib() -> ctypes.CDLL:
         L.pkv_copy_blocks.restype = ctypes.c_int
         L.pkv_merge_attention_states.argtypes = [vp, vp, i32, i32, i32, vp, ctypes.c_int, vp]
         L.pkv_merge_attention_states.restype = ctypes.c_int
+        L.pkv_cascade_workspace_size.argtypes = [dims_p, i32, i32, i32]
+        L.pkv_cascade_workspace_size.restype = sz
+        L.pkv_cascade_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                         ctypes.c_float, vp, dims_p, vp, sz, vp]
+        L.pkv_cascade_decode.restype = ctypes.c_int
         L.pkv_read_probe.argtypes = [vp, vp, i64, vp, vp]
         L.pkv_read_probe.restype = ctypes.c_int
         L.pkv_status_string.argtypes = [i32]
@@ -320,6 +325,76 @@ def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
     return _decode(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
                    out, max_seq_len, partition_size, kernel, waves_per_group,
                    balance_partitions, stream_waves, workspace, stream)
+
+
+def cascade_workspace_size(q, k_cache, block_tables, num_groups: int, max_prefix_len: int, *,
+                           max_seq_len=None, out_dtype=torch.bfloat16) -> int:
+    dims = _dims(q, k_cache, block_tables, max_seq_len, 0, out_dtype, "auto", 0, False)
+    n = lib().pkv_cascade_workspace_size(ctypes.byref(dims), int(num_groups),
+                                         int(max_prefix_len), k_cache.shape[2])
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID, "pkv_cascade_workspace_size")
+    return int(n)
+
+
+_cascade_ws = {}
+
+
+def cascade_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                   group_starts: torch.Tensor, prefix_lens: torch.Tensor, block_size: int,
+                   scale: float, out: torch.Tensor, *, max_prefix_len: int,
+                   max_seq_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Shared-prefix decode ([PU §共享前缀，分叉时 Copy-on-write]; [PU §按 Block
+    分配]): the same result as :func:`paged_attention_decode`, with the blocks
+    a group of sequences shares read once per group.  Group g is the
+    sequences ``group_starts[g] .. group_starts[g+1]-1`` (int32 [NG+1] on the
+    device), sharing their first ``prefix_lens[g]`` tokens (int32 [NG], whole
+    blocks); :meth:`BlockManager.shared_prefix_groups` derives both from the
+    tables.  ``workspace`` is a uint8 device tensor (default: one per device,
+    grown as needed); it needs no initialisation."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(v_cache, "v_cache", torch.bfloat16, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(seq_lens, "seq_lens", torch.int32, 1)
+    _check(group_starts, "group_starts", torch.int32, 1)
+    _check(prefix_lens, "prefix_lens", torch.int32, 1)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, "out", out.dtype, 3)
+    s, hq, d = q.shape
+    p, hkv, bs, d2 = k_cache.shape
+    if bs != block_size or d2 != d or tuple(v_cache.shape) != (p, hkv, d, bs):
+        raise ValueError("cache shapes must be k [P,Hkv,B,D] and v [P,Hkv,D,B] matching q")
+    if tuple(out.shape) != (s, hq, d) or block_tables.shape[0] != s or seq_lens.shape[0] != s:
+        raise ValueError("q, out, block_tables and seq_lens disagree on the batch")
+    ng = prefix_lens.shape[0]
+    if group_starts.shape[0] != ng + 1:
+        raise ValueError("group_starts must hold num_groups + 1 entries")
+    dims = _dims(q, k_cache, block_tables, max_seq_len, 0, out.dtype, "auto", 0, False)
+    L = lib()
+    need = L.pkv_cascade_workspace_size(ctypes.byref(dims), ng, int(max_prefix_len), bs)
+    if need == ctypes.c_size_t(-1).value:
+        raise PagedKVError(PKV_ERR_INVALID, "pkv_cascade_decode")
+    if workspace is None:
+        key = (q.device.type, q.device.index)
+        workspace = _cascade_ws.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1 << 20), dtype=torch.uint8, device=q.device)
+            _cascade_ws[key] = workspace
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or workspace.numel() < need:
+        raise ValueError(f"workspace must be a uint8 device tensor of at least {need} bytes")
+    st = L.pkv_cascade_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                              block_tables.data_ptr(), seq_lens.data_ptr(),
+                              group_starts.data_ptr(), prefix_lens.data_ptr(), ng,
+                              int(max_prefix_len), bs, float(scale), out.data_ptr(),
+                              ctypes.byref(dims), workspace.data_ptr(), workspace.numel(),
+                              _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_cascade_decode")
+    return out
 
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,

@@ -88,6 +88,40 @@ class BlockManager:
             arr[i, :len(t)] = t
         return arr
 
+    def shared_prefix_groups(self, seqs: Sequence) -> Tuple[np.ndarray, np.ndarray]:
+        """Groups for shared-prefix decode over the batch ``seqs`` (in batch
+        order): runs of consecutive sequences whose tables start with the same
+        physical blocks ([PU §共享前缀，分叉时 Copy-on-write]: forks of one
+        prompt point at the prompt's blocks).  A group's prefix is the leading
+        blocks that every member holds, identical and full in every member
+        (a partly filled block is never shared for long: the first divergent
+        write copies it).  Returns (group_starts int32 [NG+1], prefix_lens
+        int32 [NG], in tokens); a sequence sharing nothing with its neighbours
+        is a group of one with prefix 0."""
+        bs = self.block_size
+        starts: List[int] = [0]
+        plens: List[int] = []
+        i, n = 0, len(seqs)
+        while i < n:
+            t0 = self._tables[seqs[i]]
+            full0 = self._lengths[seqs[i]] // bs
+            common = min(len(t0), full0)
+            j = i + 1
+            while j < n:
+                tj = self._tables[seqs[j]]
+                k = min(common, len(tj), self._lengths[seqs[j]] // bs)
+                m = 0
+                while m < k and tj[m] == t0[m]:
+                    m += 1
+                if m == 0:
+                    break
+                common = m
+                j += 1
+            plens.append(common * bs if j - i > 1 else 0)
+            starts.append(j)
+            i = j
+        return np.asarray(starts, dtype=np.int32), np.asarray(plens, dtype=np.int32)
+
     # -- mutations -----------------------------------------------------------
     def _pop(self, n: int = 1) -> List[int]:
         if n > len(self._free):

@@ -406,3 +406,129 @@ pkv_status pkv_merge_attention_states(const float* part_out, const float* part_l
 }
 
 }  // extern "C"
+
+namespace {
+
+// Shared-prefix decode: items and workspace regions for the host bounds.
+struct CascadePlan {
+  bool ok;
+  pkv_status status;
+  int32_t group;
+  int64_t max_pre_items, max_suf_items;
+  int32_t waves;
+  // workspace: [pre_acc | pre_ml | suf_acc | suf_ml | tables]
+  size_t pre_ml_offset, suf_acc_offset, suf_ml_offset, tables_offset, workspace_bytes;
+};
+
+CascadePlan plan_cascade(const pkv_decode_dims* d, int32_t num_groups, int32_t max_prefix_len,
+                         int32_t block_size) {
+  CascadePlan p = {};
+  p.status = PKV_ERR_INVALID;
+  if (d == nullptr) return p;
+  if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 ||
+      block_size < 1 || d->num_blocks < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 0)
+    return p;
+  if (d->num_q_heads % d->num_kv_heads != 0) return p;
+  if (static_cast<int64_t>(d->max_seq_len) >
+      static_cast<int64_t>(d->max_blocks_per_seq) * block_size)
+    return p;
+  if (d->out_dtype != PKV_DTYPE_BF16 && d->out_dtype != PKV_DTYPE_F32) return p;
+  if (num_groups < 0 || (d->num_seqs > 0 && (num_groups < 1 || num_groups > d->num_seqs)))
+    return p;
+  if (max_prefix_len < 0 || max_prefix_len > d->max_seq_len) return p;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  if (!pkv::cascade_shape_supported(d->head_dim, block_size, p.group, d->num_seqs))
+    return (p.status = PKV_ERR_UNSUPPORTED, p);
+  const int64_t S = d->num_seqs, NG = num_groups, Hkv = d->num_kv_heads, G = p.group;
+  const int64_t D = d->head_dim;
+  auto div_up = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  const int64_t seg_p = div_up(div_up(max_prefix_len, 32), pkv::kCascadePrefixChunks);
+  const int64_t seg_s = div_up(div_up(d->max_seq_len, 32), pkv::kCascadeSuffixChunks);
+  // row blocks over all groups: sum_g ceil(F_g G / rows) <= NG + ceil(S G / rows)
+  const int64_t rows = pkv::kCascadeRows;
+  p.max_pre_items = Hkv * seg_p * (NG + div_up(S * G, rows));
+  p.max_suf_items = S * Hkv * seg_s;
+  if (p.max_pre_items + p.max_suf_items > 0x7FFFFFFF) return (p.status = PKV_ERR_UNSUPPORTED, p);
+  // launch 1: every wavefront resident on an MI355X (2 per SIMD at head_dim 64,
+  // 1 at 128), fewer when there are fewer items
+  const int64_t target = D <= 64 ? 2048 : 1024;
+  int64_t waves = p.max_pre_items + p.max_suf_items;
+  waves = waves < target ? waves : target;
+  waves = (waves + 3) / 4 * 4;
+  p.waves = static_cast<int32_t>(waves < 4 ? 4 : waves);
+  const size_t pre_acc = round_up(static_cast<size_t>(p.max_pre_items) * rows * D * 4, kAlign);
+  const size_t pre_ml = round_up(static_cast<size_t>(p.max_pre_items) * rows * 2 * 4, kAlign);
+  const size_t suf_acc = round_up(static_cast<size_t>(p.max_suf_items) * G * D * 4, kAlign);
+  const size_t suf_ml = round_up(static_cast<size_t>(p.max_suf_items) * G * 2 * 4, kAlign);
+  const size_t tables = round_up(static_cast<size_t>(pkv::kCascadeTableHead + 8 * S) * 4, kAlign);
+  p.pre_ml_offset = pre_acc;
+  p.suf_acc_offset = p.pre_ml_offset + pre_ml;
+  p.suf_ml_offset = p.suf_acc_offset + suf_acc;
+  p.tables_offset = p.suf_ml_offset + suf_ml;
+  p.workspace_bytes = p.tables_offset + tables;
+  p.ok = true;
+  p.status = PKV_OK;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_cascade_workspace_size(const pkv_decode_dims* dims, int32_t num_groups,
+                                  int32_t max_prefix_len, int32_t block_size) {
+  const CascadePlan p = plan_cascade(dims, num_groups, max_prefix_len, block_size);
+  if (!p.ok) return static_cast<size_t>(-1);
+  return p.workspace_bytes;
+}
+
+pkv_status pkv_cascade_decode(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              const int32_t* group_starts, const int32_t* prefix_lens,
+                              int32_t num_groups, int32_t max_prefix_len, int32_t block_size,
+                              float scale, void* out, const pkv_decode_dims* dims,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  const CascadePlan p = plan_cascade(dims, num_groups, max_prefix_len, block_size);
+  if (!p.ok) return p.status;
+  if (dims->num_seqs == 0) return PKV_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
+      seq_lens == nullptr || group_starts == nullptr || prefix_lens == nullptr || out == nullptr)
+    return PKV_ERR_INVALID;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
+  if (workspace == nullptr || workspace_bytes < p.workspace_bytes) return PKV_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PKV_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  pkv::CascadeLaunch a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.group_starts = group_starts;
+  a.prefix_lens = prefix_lens;
+  a.num_seqs = dims->num_seqs;
+  a.num_groups = num_groups;
+  a.num_q_heads = dims->num_q_heads;
+  a.num_kv_heads = dims->num_kv_heads;
+  a.group = p.group;
+  a.head_dim = dims->head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = dims->max_blocks_per_seq;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  a.out_f32 = dims->out_dtype == PKV_DTYPE_F32 ? 1 : 0;
+  a.out = out;
+  a.pre_acc = reinterpret_cast<float*>(ws);
+  a.pre_ml = reinterpret_cast<float*>(ws + p.pre_ml_offset);
+  a.suf_acc = reinterpret_cast<float*>(ws + p.suf_acc_offset);
+  a.suf_ml = reinterpret_cast<float*>(ws + p.suf_ml_offset);
+  a.tables = reinterpret_cast<int32_t*>(ws + p.tables_offset);
+  a.max_prefix_len = max_prefix_len;
+  a.max_seq_len = dims->max_seq_len;
+  a.max_pre_items = p.max_pre_items;
+  a.max_suf_items = p.max_suf_items;
+  a.waves = p.waves;
+  return hip_status(pkv::launch_cascade(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

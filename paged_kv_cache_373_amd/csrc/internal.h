@@ -110,4 +110,45 @@ hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int3
                               const int32_t* block_pairs, int32_t num_pairs,
                               int64_t block_bytes, hipStream_t stream);
 
+// Shared-prefix (cascade) decode.  Groups are contiguous runs of sequences,
+// group g = [group_starts[g], group_starts[g+1]), sharing their first
+// prefix_lens[g] tokens (whole blocks).  Launch 1 folds items into partial
+// states: a prefix item is kCascadePrefixChunks 32-token chunks of a group's
+// prefix for one block of kCascadeRows query rows (member-major, G heads
+// each), a suffix item is kCascadeSuffixChunks chunks of one sequence's tokens
+// past the prefix.  Launch 2 merges, per (sequence, KV head), the partials of
+// its group's prefix items and of its own suffix items.
+constexpr int kCascadeRows = 16;           // query rows of a prefix item: one matrix-core tile
+constexpr int kCascadePrefixChunks = 4;    // chunks per prefix item
+constexpr int kCascadeSuffixChunks = 4;    // chunks per suffix item
+constexpr int kCascadeMaxSeqs = 4096;      // sequences (and groups) per call
+constexpr int kCascadeTableHead = 4;       // status word and padding before the item tables
+struct CascadeLaunch {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* group_starts;  // [NG + 1]
+  const int32_t* prefix_lens;   // [NG]
+  int32_t num_seqs, num_groups, num_q_heads, num_kv_heads, group, head_dim, block_size;
+  int32_t max_blocks_per_seq;
+  float scale_log2;
+  int32_t out_f32;
+  void* out;
+  float* pre_acc;   // [max_pre_items][kCascadeRows][D]
+  float* pre_ml;    // [max_pre_items][kCascadeRows][max, sum]
+  float* suf_acc;   // [max_suf_items][G][D]
+  float* suf_ml;    // [max_suf_items][G][max, sum]
+  int32_t* tables;  // [kCascadeTableHead + 8 S]: status, then per sequence its merge
+                    // descriptor (first prefix item of its group, row blocks, prefix
+                    // items per row block, member index, first suffix item, suffix
+                    // items per head, 2 spare)
+  int32_t max_prefix_len, max_seq_len;  // host bounds the device lengths are checked against
+  int64_t max_pre_items, max_suf_items;
+  int32_t waves;    // launch 1 wavefronts (a multiple of 4)
+};
+bool cascade_shape_supported(int head_dim, int block_size, int group, int num_seqs);
+hipError_t launch_cascade(const CascadeLaunch& a, hipStream_t stream);
+
 }  // namespace pkv

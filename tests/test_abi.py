@@ -243,3 +243,55 @@ def test_writers_reject_before_any_hip_call():
     assert lib.pkv_merge_attention_states(f, f, 4, 0, 64, f, 0, None) == pkv.PKV_ERR_INVALID
     assert lib.pkv_merge_attention_states(f, f, 4, 2, 300, f, 0, None) == pkv.PKV_ERR_INVALID
     assert lib.pkv_merge_attention_states(f, f, 0, 2, 64, f, 0, None) == pkv.PKV_OK
+
+
+def cws(dims, ng, lp, bs=16):
+    return pkv.lib().pkv_cascade_workspace_size(ctypes.byref(dims), ng, lp, bs)
+
+
+def test_cascade_workspace_size_rules():
+    # S=2, Hkv=8, G=4, D=64, max 64 tokens, prefix bound 32: 1 prefix segment,
+    # 1 suffix segment (4 chunks of 32); prefix items hold 16 query rows
+    region = lambda n: (n + 255) // 256 * 256
+    d = _dims()
+    pre = 8 * 1 * (1 + -(-2 * 4 // 16))  # Hkv x segments x (groups + row blocks of S G rows)
+    suf = 2 * 8 * 1
+    expect = (region(pre * 16 * 64 * 4) + region(pre * 16 * 2 * 4) + region(suf * 4 * 64 * 4)
+              + region(suf * 4 * 2 * 4) + region((4 + 8 * 2) * 4))
+    assert cws(d, 1, 32) == expect
+    d128 = _dims(head_dim=128)
+    pre128 = 8 * 1 * (2 + -(-2 * 4 // 16))
+    assert cws(d128, 2, 32) == (region(pre128 * 16 * 128 * 4) + region(pre128 * 16 * 2 * 4)
+                                + region(suf * 4 * 128 * 4) + region(suf * 4 * 2 * 4)
+                                + region((4 + 8 * 2) * 4))
+    assert cws(d, 0, 32) == BAD  # S > 0 needs a group
+    assert cws(d, 3, 32) == BAD  # more groups than sequences
+    assert cws(d, 1, 65) == BAD  # prefix bound above max_seq_len
+    assert cws(d, 1, -1) == BAD
+    assert cws(_dims(head_dim=80), 1, 32) == BAD  # matrix-core shapes only
+    assert cws(_dims(num_q_heads=32, num_kv_heads=1), 1, 32) == BAD  # G = 32 > 16
+    assert cws(_dims(num_seqs=5000, max_blocks_per_seq=4), 1, 32) == BAD  # S > 4096
+    assert cws(_dims(num_seqs=0), 0, 0) >= 0
+
+
+def test_cascade_rejects_before_any_hip_call():
+    lib = pkv.lib()
+    dims = _dims()
+    f = ctypes.c_void_p(0x1000)
+    need = cws(dims, 1, 32)
+
+    def call(q=f, gs=f, pl=f, ng=1, lp=32, scale=0.125, ws=f, wsb=need, d=dims):
+        return lib.pkv_cascade_decode(q, f, f, f, f, gs, pl, ng, lp, 16, scale, f,
+                                      ctypes.byref(d), ws, wsb, None)
+    assert call(q=None) == pkv.PKV_ERR_INVALID
+    assert call(gs=None) == pkv.PKV_ERR_INVALID
+    assert call(pl=None) == pkv.PKV_ERR_INVALID
+    assert call(ng=0) == pkv.PKV_ERR_INVALID
+    assert call(lp=100) == pkv.PKV_ERR_INVALID
+    assert call(scale=float("inf")) == pkv.PKV_ERR_INVALID
+    assert call(q=ctypes.c_void_p(0x1002)) == pkv.PKV_ERR_INVALID
+    assert call(ws=None) == pkv.PKV_ERR_WORKSPACE
+    assert call(wsb=need - 1) == pkv.PKV_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x1010)) == pkv.PKV_ERR_WORKSPACE  # not 256-aligned
+    assert call(d=_dims(head_dim=80)) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(d=_dims(num_seqs=0), ng=0, lp=0) == pkv.PKV_OK  # nothing to do

@@ -125,3 +125,38 @@ def test_random_trace_agrees_with_oracle_model(seed):
             assert bm.table(s) == om.tables[s]
         assert list(bm._free) == om.free
         assert bm.refcount.tolist() == om.ref
+
+
+def test_shared_prefix_groups():
+    """Forks of one prompt form a group whose prefix is the leading blocks all
+    members hold, identical and full; a partly filled shared tail is not part
+    of it, and a sequence sharing nothing is a group of one with prefix 0."""
+    bm = BlockManager(200, 4)
+    bm.add_sequence("p")
+    bm.append_tokens("p", 10)  # blocks 0, 1 full, block 2 holds 2 tokens
+    for f in range(3):
+        bm.fork("p", f)
+    bm.release("p")
+    for f in range(3):
+        bm.append_tokens(f, f + 1)  # forks 0, 1 copy the shared tail, fork 2 takes it
+    bm.add_sequence("x")
+    bm.append_tokens("x", 5)
+    bm.add_sequence("y")
+    bm.append_tokens("y", 3)
+    bm.fork("y", "y2")
+    gs, pl = bm.shared_prefix_groups([0, 1, 2, "x", "y", "y2"])
+    # the forks share blocks 0 and 1 (8 tokens); "y" and "y2" share only a
+    # partly filled block, so each is a group of one
+    assert gs.tolist() == [0, 3, 4, 5, 6]
+    assert pl.tolist() == [8, 0, 0, 0]
+    assert gs.dtype == np.int32 and pl.dtype == np.int32
+    # a member shorter than the others bounds the group's prefix by its full blocks
+    bm.add_sequence("z")
+    bm.append_tokens("z", 12)
+    bm.fork("z", "z2")
+    bm.append_tokens("z", 9)
+    gs, pl = bm.shared_prefix_groups(["z", "z2"])
+    assert gs.tolist() == [0, 2] and pl.tolist() == [12]
+    # order matters: groups are runs of neighbours
+    gs, pl = bm.shared_prefix_groups([0, "x", 1])
+    assert gs.tolist() == [0, 1, 2, 3] and pl.tolist() == [0, 0, 0]

@@ -291,3 +291,63 @@ def random_small(seed: int, num_seqs: int, hq: int, hkv: int, d: int, bs: int,
     return Workload(f"random{seed}", wid, hq, hkv, d, bs, pool, lens, q,
                     1.0 / math.sqrt(d), block_tables=bt, k_tok=k, v_tok=v,
                     poison_block=poison)
+
+
+def shared_prefix_small(seed: int, group_sizes: List[int], prefix_blocks: List[int], hq: int,
+                        hkv: int, d: int, bs: int, max_suffix: int, min_suffix: int = 0,
+                        empty_tail: bool = False) -> Workload:
+    """Small shared-prefix case: group g is group_sizes[g] consecutive
+    sequences whose tables start with the same prefix_blocks[g] physical
+    blocks (the group's prompt, drawn once), each followed by a private
+    suffix of U{min_suffix..max_suffix} tokens in blocks of its own.  With
+    ``empty_tail`` a last group of one empty sequence is appended.  Blocks are
+    a seeded permutation of the pool.  k_tok/v_tok hold every sequence's full
+    logical sequence (the prompt rows repeated per member); ``extra`` holds
+    group_starts, prefix_lens and ``repeat_rows``, the k_tok rows that repeat a
+    prompt row already held by the group's first member."""
+    wid = 101
+    sizes = list(group_sizes) + ([1] if empty_tail else [])
+    pblocks = list(prefix_blocks) + ([0] if empty_tail else [])
+    s = sum(sizes)
+    suf = rng(wid, _ROLE_PRIV_LEN, seed).integers(min_suffix, max_suffix, size=s,
+                                                  endpoint=True).astype(np.int32)
+    if empty_tail:
+        suf[-1] = 0
+    owner = np.repeat(np.arange(len(sizes)), sizes)
+    lens = (np.asarray(pblocks, dtype=np.int32)[owner] * bs + suf).astype(np.int32)
+    need = sum(pblocks) + sum(int(math.ceil(int(x) / bs)) for x in suf)
+    pool = need + 3
+    perm = rng(wid, _ROLE_PERM, seed).permutation(pool).astype(np.int32)
+    pos = 0
+    rows: List[List[int]] = []
+    prompts_k, prompts_v = [], []
+    for g, (n, pb) in enumerate(zip(sizes, pblocks)):
+        shared = perm[pos:pos + pb].tolist()
+        pos += pb
+        prompts_k.append(normal_bf16(rng(wid, _ROLE_K, seed, g), (pb * bs, hkv, d)))
+        prompts_v.append(normal_bf16(rng(wid, _ROLE_V, seed, g), (pb * bs, hkv, d)))
+        for _ in range(n):
+            b = len(rows)
+            nb = int(math.ceil(int(suf[b]) / bs))
+            rows.append(shared + perm[pos:pos + nb].tolist())
+            pos += nb
+    poison = int(perm[pos])
+    width = max(max(len(r) for r in rows), 1)
+    bt = _pad_tables(rows, width, poison)
+    ks, vs, repeat = [], [], []
+    starts = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    for b in range(s):
+        g = int(owner[b])
+        ks.append(prompts_k[g])
+        vs.append(prompts_v[g])
+        repeat.append(np.full(len(prompts_k[g]), b != starts[g]))
+        ks.append(normal_bf16(rng(wid, _ROLE_K, seed, 1000 + b), (int(suf[b]), hkv, d)))
+        vs.append(normal_bf16(rng(wid, _ROLE_V, seed, 1000 + b), (int(suf[b]), hkv, d)))
+        repeat.append(np.zeros(int(suf[b]), bool))
+    q = normal_bf16(rng(wid, _ROLE_Q, seed), (s, hq, d))
+    return Workload(f"shared_prefix{seed}", wid, hq, hkv, d, bs, pool, lens, q,
+                    1.0 / math.sqrt(d), block_tables=bt, k_tok=np.concatenate(ks),
+                    v_tok=np.concatenate(vs), poison_block=poison,
+                    extra=dict(group_starts=starts,
+                               prefix_lens=(np.asarray(pblocks) * bs).astype(np.int32),
+                               repeat_rows=np.concatenate(repeat)))
