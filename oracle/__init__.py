@@ -24,6 +24,10 @@ Everything here is a plain, direct statement of what those pages define:
 * :func:`paged_decode` / :func:`dense_decode` - gather K,V into position order
   and run dense softmax attention in fp64 (the C file ``pkv_oracle.c``);
   :func:`paged_decode_py` is the same in pure Python for tiny inputs.
+* :func:`paged_prefill` - the causal multi-query form: each new token of a
+  sequence attends the positions up to its own ([PU §KV Cache 为什么会浪费
+  显存]: causal attention; [PU §Continuous Batching]: paging keeps the dense
+  attention semantics); :func:`paged_prefill_py` in pure Python.
 
 Cache layout (the library's documented layout, restated independently):
 k_cache bf16 [P, Hkv, B, D], v_cache bf16 [P, Hkv, D, B] (numpy C order).
@@ -235,6 +239,9 @@ def _load():
         lib.oracle_dense_decode.argtypes = [u16p, u16p, u16p, i64p, i32, i32, i32, i32,
                                             ctypes.c_double, f64p, i32]
         lib.oracle_dense_decode.restype = ctypes.c_int
+        lib.oracle_paged_prefill.argtypes = [u16p, u16p, u16p, i32p, i32p, i64p, i32, i32, i32,
+                                             i32, i32, i32, ctypes.c_double, f64p, i32]
+        lib.oracle_paged_prefill.restype = ctypes.c_int
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -290,6 +297,72 @@ def dense_decode(q: np.ndarray, k_tok: np.ndarray, v_tok: np.ndarray,
                                  int(num_threads))
     if rc != 0:
         raise RuntimeError(f"oracle_dense_decode failed: {rc}")
+    return out
+
+
+def paged_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                  block_tables: np.ndarray, seq_lens: np.ndarray, q_lens: np.ndarray,
+                  scale: float, num_threads: int = 0) -> np.ndarray:
+    """fp64 [N, Hq, D]: causal multi-query attention of every sequence's new
+    tokens (the last q_lens[b] of its seq_lens[b] cached tokens; q rows
+    sequence-major) through the tables.  New token i of sequence b sits at
+    position T_b - q_len_b + i and sees positions 0 .. that one ([PU §KV Cache
+    为什么会浪费显存]: causal attention; [PU §Continuous Batching]: dense
+    attention semantics are kept over the paged layout)."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    k_cache = np.ascontiguousarray(k_cache, dtype=np.uint16)
+    v_cache = np.ascontiguousarray(v_cache, dtype=np.uint16)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    ql = np.asarray(q_lens, dtype=np.int64)
+    cu = np.zeros(ql.shape[0] + 1, dtype=np.int64)
+    np.cumsum(ql, out=cu[1:])
+    n, hq, d = q.shape
+    assert n == cu[-1]
+    _, hkv, bs, d2 = k_cache.shape
+    assert d2 == d and v_cache.shape == (k_cache.shape[0], hkv, d, bs)
+    out = np.zeros((n, hq, d), dtype=np.float64)
+    rc = lib.oracle_paged_prefill(_ptr(q, ctypes.c_uint16), _ptr(k_cache, ctypes.c_uint16),
+                                  _ptr(v_cache, ctypes.c_uint16), _ptr(bt, ctypes.c_int32),
+                                  _ptr(lens, ctypes.c_int32), _ptr(cu, ctypes.c_int64),
+                                  lens.shape[0], hq, hkv, d, bs, bt.shape[1], float(scale),
+                                  _ptr(out, ctypes.c_double), int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_paged_prefill failed: {rc}")
+    return out
+
+
+def paged_prefill_py(q, k_cache, v_cache, block_tables, seq_lens, q_lens, scale) -> np.ndarray:
+    """Pure-Python loops, for tiny inputs only: the causal prefill definition
+    of :func:`paged_prefill` written a second time, each token's row from its
+    own scores."""
+    hq, d = q.shape[1], q.shape[2]
+    hkv = k_cache.shape[1]
+    group = hq // hkv
+    out = np.zeros(q.shape, dtype=np.float64)
+    row = 0
+    for b in range(len(seq_lens)):
+        length, nq = int(seq_lens[b]), int(q_lens[b])
+        kb, vb = gather(k_cache, v_cache, block_tables[b], length)
+        kf, vf = widen_bf16(kb), widen_bf16(vb)
+        for i in range(nq):
+            pos = length - nq + i
+            qf = widen_bf16(q[row])
+            for h in range(hq):
+                kv = h // group
+                scores = []
+                for t in range(pos + 1):
+                    acc = 0.0
+                    for j in range(d):
+                        acc += float(qf[h, j]) * float(kf[t, kv, j])
+                    scores.append(scale * acc)
+                m = max(scores)
+                e = [math.exp(x - m) for x in scores]
+                z = sum(e)
+                for j in range(d):
+                    out[row, h, j] = sum(e[t] * float(vf[t, kv, j]) for t in range(pos + 1)) / z
+            row += 1
     return out
 
 

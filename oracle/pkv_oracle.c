@@ -1,6 +1,6 @@
 /*
  * pkv_oracle.c - TEST INFRASTRUCTURE.  The CPU oracle for paged decode
- * attention.  Only tests, the smoke check and the benchmark's CPU-baseline
+ * attention (and the causal multi-query prefill over the same cache).  Only tests, the smoke check and the benchmark's CPU-baseline
  * leg may load this file's library; the product path never does.
  *
  * What it computes is the plain definition the pages give, written out with
@@ -153,6 +153,68 @@ int oracle_dense_decode(const uint16_t* q, const uint16_t* k_tok, const uint16_t
           qrow[d] = widen_bf16(q[((int64_t)b * Hq + hq) * D + d]);
         dense_attention_row(qrow, K, V, T, D, D, scale, s,
                             out + ((int64_t)b * Hq + hq) * D);
+      }
+    }
+    free(K);
+    free(V);
+    free(s);
+    free(qrow);
+  }
+  return status;
+}
+
+/* Paged prefill (causal multi-query) attention.  The new tokens of sequence b
+ * are the last q_len_b = cu_q[b+1] - cu_q[b] of its T_b cached tokens (their
+ * K,V already in the cache); new token i sits at position p = T_b - q_len_b + i
+ * and, as causal attention, sees the tokens at positions 0 .. p ([PU] "KV
+ * Cache 为什么会浪费显存": in causal attention a token attends to the tokens
+ * before it, whose K,V the cache keeps; [PU] "Continuous Batching": paging
+ * and FlashAttention both keep the dense attention semantics).  So each new
+ * token's row is the dense attention above over the first p + 1 gathered rows.
+ * q bf16 [N, Hq, D] (N = cu_q[S]), out fp64 [N, Hq, D].  Returns 0, or -1 on
+ * bad sizes (including q_len_b > T_b), -2 on allocation failure. */
+int oracle_paged_prefill(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int64_t* cu_q, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t B, int32_t max_blocks, double scale, double* out,
+                         int32_t num_threads) {
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B <= 0) return -1;
+  for (int32_t b = 0; b < S; b++)
+    if (cu_q[b + 1] - cu_q[b] < 0 || cu_q[b + 1] - cu_q[b] > seq_lens[b]) return -1;
+  const int32_t G = Hq / Hkv;
+  const int64_t units = (int64_t)S * Hkv;
+  int status = 0;
+#ifdef _OPENMP
+  if (num_threads <= 0) num_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads)
+#endif
+  for (int64_t u = 0; u < units; u++) {
+    const int32_t b = (int32_t)(u / Hkv), h = (int32_t)(u % Hkv);
+    const int64_t T = seq_lens[b];
+    const int64_t nq = cu_q[b + 1] - cu_q[b];
+    double* K = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * D);
+    double* V = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * D);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!K || !V || !s || !qrow) {
+      status = -2;
+    } else {
+      for (int64_t t = 0; t < T; t++) {
+        const int64_t p = block_tables[(int64_t)b * max_blocks + t / B];
+        const int64_t o = t % B;
+        for (int32_t d = 0; d < D; d++) {
+          K[t * D + d] = widen_bf16(k_cache[((p * Hkv + h) * B + o) * D + d]);
+          V[t * D + d] = widen_bf16(v_cache[((p * Hkv + h) * D + d) * B + o]);
+        }
+      }
+      for (int64_t i = 0; i < nq; i++) {
+        const int64_t pos = T - nq + i; /* this token's position */
+        const int64_t n = cu_q[b] + i;  /* its row in q and out */
+        for (int32_t g = 0; g < G; g++) {
+          const int32_t hq = h * G + g;
+          for (int32_t d = 0; d < D; d++) qrow[d] = widen_bf16(q[(n * Hq + hq) * D + d]);
+          dense_attention_row(qrow, K, V, pos + 1, D, D, scale, s, out + (n * Hq + hq) * D);
+        }
       }
     }
     free(K);

@@ -349,3 +349,91 @@ def test_bf16_round_matches_torch():
     x = np.concatenate([r.normal(size=5000) * 10, [0.0, -0.0, 1e-40, 3.0e38]])
     want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     np.testing.assert_array_equal(oracle.bf16_round(x), want)
+
+
+# ---------------------------------------------------------------- prefill
+
+
+def _sdpa_prefill_f64(w):
+    """torch's own attention routine (fp64, CPU) with an explicit causal mask
+    aligned to the end of each sequence: new token i of sequence b may see
+    positions 0 .. ctx_b + i."""
+    ql = w.extra["q_lens"]
+    out = np.zeros(w.q.shape, dtype=np.float64)
+    cu = w.cu_seqlens
+    qf = oracle.widen_bf16(w.q)
+    row = 0
+    for b in range(w.num_seqs):
+        T, n = int(w.seq_lens[b]), int(ql[b])
+        k = torch.from_numpy(oracle.widen_bf16(w.k_tok[cu[b]:cu[b + 1]])).permute(1, 0, 2)
+        v = torch.from_numpy(oracle.widen_bf16(w.v_tok[cu[b]:cu[b + 1]])).permute(1, 0, 2)
+        q = torch.from_numpy(qf[row:row + n]).permute(1, 0, 2)
+        mask = torch.arange(T)[None, :] <= (T - n + torch.arange(n))[:, None]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[None], k[None].contiguous(), v[None].contiguous(), attn_mask=mask,
+            scale=w.scale, enable_gqa=True)
+        out[row:row + n] = o[0].permute(1, 0, 2).numpy()
+        row += n
+    return out
+
+
+PREFILL_CASES = [
+    lambda: workloads.prefill_small(1, 3, 4, 2, 16, 4, 20, 9),
+    lambda: workloads.prefill_small(2, 4, 8, 2, 32, 8, 40, 17, min_ctx=0),
+    lambda: workloads.prefill_small(3, 2, 6, 6, 8, 3, 0, 12),   # no context: a whole prompt
+    lambda: workloads.prefill_small(4, 5, 16, 1, 24, 16, 70, 5),
+]
+
+
+@pytest.mark.parametrize("make", PREFILL_CASES)
+def test_prefill_oracle_matches_torch_sdpa(make):
+    w = make()
+    kc, vc = _oracle_cache(w)
+    got = oracle.paged_prefill(w.q, kc, vc, w.block_tables, w.seq_lens, w.extra["q_lens"],
+                               w.scale)
+    np.testing.assert_allclose(got, _sdpa_prefill_f64(w), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("make", PREFILL_CASES[:3])
+def test_prefill_oracle_matches_brute_force(make):
+    w = make()
+    kc, vc = _oracle_cache(w)
+    args = (w.q, kc, vc, w.block_tables, w.seq_lens, w.extra["q_lens"], w.scale)
+    np.testing.assert_allclose(oracle.paged_prefill(*args), oracle.paged_prefill_py(*args),
+                               rtol=1e-13, atol=1e-14)
+
+
+def test_prefill_of_one_token_is_decode():
+    """A chunk of one new token per sequence is the decode step."""
+    w = workloads.random_small(5, 6, 8, 2, 32, 4, 30, min_len=1)
+    kc, vc = _oracle_cache(w)
+    got = oracle.paged_prefill(w.q, kc, vc, w.block_tables, w.seq_lens,
+                               np.ones(w.num_seqs, np.int32), w.scale)
+    want = oracle.paged_decode(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_prefill_first_position_returns_v0_and_future_is_invisible():
+    """With no context the first new token sees only itself (its output is
+    v_0 exactly); changing the K/V of later positions leaves every earlier
+    token's output unchanged, bit for bit."""
+    w = workloads.prefill_small(6, 3, 4, 2, 16, 4, 0, 10, min_q=3)
+    kc, vc = _oracle_cache(w)
+    ql = w.extra["q_lens"]
+    args = lambda kc_, vc_: (w.q, kc_, vc_, w.block_tables, w.seq_lens, ql, w.scale)
+    out = oracle.paged_prefill(*args(kc, vc))
+    cu_q = np.concatenate([[0], np.cumsum(ql)])
+    cu = w.cu_seqlens
+    for b in range(w.num_seqs):
+        v0 = oracle.widen_bf16(w.v_tok[cu[b]])  # [Hkv, D]
+        np.testing.assert_array_equal(out[cu_q[b]], np.repeat(v0, 2, axis=0))
+    # perturb the last position of sequence 0: only its own last row may change
+    kc2, vc2 = kc.copy(), vc.copy()
+    last = int(w.seq_lens[0]) - 1
+    s = oracle.slot(w.block_tables[0], last, w.block_size)
+    kc2[s // w.block_size, :, s % w.block_size, :] ^= np.uint16(0x0040)
+    vc2[s // w.block_size, :, :, s % w.block_size] ^= np.uint16(0x0040)
+    out2 = oracle.paged_prefill(*args(kc2, vc2))
+    np.testing.assert_array_equal(out2[:cu_q[1] - 1], out[:cu_q[1] - 1])
+    np.testing.assert_array_equal(out2[cu_q[1]:], out[cu_q[1]:])
+    assert not np.array_equal(out2[cu_q[1] - 1], out[cu_q[1] - 1])

@@ -351,3 +351,52 @@ def shared_prefix_small(seed: int, group_sizes: List[int], prefix_blocks: List[i
                     extra=dict(group_starts=starts,
                                prefix_lens=(np.asarray(pblocks) * bs).astype(np.int32),
                                repeat_rows=np.concatenate(repeat)))
+
+
+def prefill_small(seed: int, num_seqs: int, hq: int, hkv: int, d: int, bs: int, max_ctx: int,
+                  max_q: int, min_q: int = 1, min_ctx: int = 0, slack_blocks: int = 3,
+                  wid: int = 102) -> Workload:
+    """Prefill / chunked-prefill case: sequence b holds ctx_b cached tokens
+    (U{min_ctx..max_ctx}) followed by q_len_b new ones (U{min_q..max_q}), all
+    T_b = ctx_b + q_len_b of them in the cache; ``q`` holds the new tokens'
+    queries, sequence-major ([sum q_len, Hq, D]); ``extra["q_lens"]`` their
+    counts.  Blocks are a seeded permutation of the pool."""
+    ctx = rng(wid, _ROLE_LENS, seed).integers(min_ctx, max_ctx, size=num_seqs,
+                                              endpoint=True).astype(np.int32)
+    ql = rng(wid, _ROLE_PRIV_LEN, seed).integers(min_q, max_q, size=num_seqs,
+                                                 endpoint=True).astype(np.int32)
+    lens = (ctx + ql).astype(np.int32)
+    need = [int(math.ceil(t / bs)) for t in lens]
+    pool = sum(need) + slack_blocks
+    perm = rng(wid, _ROLE_PERM, seed).permutation(pool).astype(np.int32)
+    rows, pos = [], 0
+    for nb in need:
+        rows.append(perm[pos:pos + nb].tolist())
+        pos += nb
+    poison = int(perm[pos])
+    bt = _pad_tables(rows, max(max(need) if need else 1, 1), poison)
+    n = int(lens.sum())
+    q = normal_bf16(rng(wid, _ROLE_Q, seed), (int(ql.sum()), hq, d))
+    k = normal_bf16(rng(wid, _ROLE_K, seed), (n, hkv, d))
+    v = normal_bf16(rng(wid, _ROLE_V, seed), (n, hkv, d))
+    return Workload(f"prefill{seed}", wid, hq, hkv, d, bs, pool, lens, q, 1.0 / math.sqrt(d),
+                    block_tables=bt, k_tok=k, v_tok=v, poison_block=poison,
+                    extra=dict(q_lens=ql))
+
+
+def prefill_chunked(num_seqs: int = 8, q_len: int = 512, max_ctx: int = 2048,
+                    wid: int = 7) -> Workload:
+    """Llama-3.2-1B-shaped chunked prefill step of one layer: 8 sequences each
+    adding a 512-token chunk after a cached context of U{0..2048} tokens (32 q
+    heads, 8 KV heads, head_dim 64, B = 16), physical blocks a seeded
+    permutation of a pool 10 % larger than needed."""
+    hq, hkv, d, bs = 32, 8, 64, 16
+    ctx = rng(wid, _ROLE_LENS).integers(0, max_ctx, size=num_seqs, endpoint=True).astype(np.int32)
+    ql = np.full(num_seqs, q_len, dtype=np.int32)
+    lens = (ctx + ql).astype(np.int32)
+    bt, pool, poison = _permuted_tables(wid, lens, bs)
+    q = normal_bf16(rng(wid, _ROLE_Q), (int(ql.sum()), hq, d))
+    k, v = _llama_shape_tokens(wid, lens, hkv, d)
+    return Workload("prefill_chunked", wid, hq, hkv, d, bs, pool, lens, q, 1.0 / math.sqrt(d),
+                    block_tables=bt, k_tok=k, v_tok=v, poison_block=poison,
+                    extra=dict(q_lens=ql))
