@@ -16,8 +16,10 @@ total) that it cannot sit in the 256 MB Infinity Cache between steps.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
 ``--workload`` is llama_b64 (default, the headline line) or long_splitkv;
-prefix_cow and pool16 print their own report lines instead (logical and
-unique GB/s with the copy_blocks time; the 16-layer pool step per block size).
+prefix_cow, pool16 and prefill_chunked print their own report lines instead
+(logical and unique GB/s with the shared-prefix decode and the copy_blocks
+time; the 16-layer pool step per block size; the chunked prefill's matrix-core
+rate).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
 GPU.  ``roofline.achieved`` is the decode launch alone (HIP events on the
@@ -308,6 +310,71 @@ def run_prefix_cow(args) -> int:
     return 0
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def run_prefill(args) -> int:
+    """The Llama-shaped chunked prefill of one layer: 8 sequences, each adding
+    512 new tokens after U{0..2048} cached ones (their K/V written first, as a
+    prefill step does); one pkv_paged_prefill launch per step.  Reports new
+    tokens per second and the attention's algorithmic matrix-core rate: per
+    new token and query head, 4 D flops per visible position (QK and PV)."""
+    import torch
+
+    import paged_kv_cache_373_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    w = workloads.prefill_chunked()
+    ql = w.extra["q_lens"]
+    n = int(ql.sum())
+    cu_np = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    ctx = w.seq_lens - ql
+    visible = int(sum(int(ql[b]) * int(ctx[b]) + int(ql[b]) * (int(ql[b]) + 1) // 2
+                      for b in range(w.num_seqs)))
+    flops = 4 * w.head_dim * w.num_q_heads * visible
+    pool_bytes = 2 * w.num_blocks * w.num_kv_heads * w.block_size * w.head_dim * 2
+    copies = args.copies or max(2, math.ceil(ROTATE_BYTES / pool_bytes))
+    seq = np.repeat(np.arange(w.num_seqs), w.seq_lens)
+    pos = np.concatenate([np.arange(t) for t in w.seq_lens])
+    from paged_kv_cache_373_amd.block_manager import slot_mapping_for
+    slots = torch.from_numpy(slot_mapping_for(w.block_tables, seq, pos, w.block_size)).to(dev)
+    kt, vt = bits_to_bf16(w.k_tok).to(dev), bits_to_bf16(w.v_tok).to(dev)
+    caches = []
+    for _ in range(copies):
+        kc, vc = pkv.new_kv_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim,
+                                  device=dev, fill=float("nan"))
+        pkv.reshape_and_cache(kt, vt, slots, kc, vc)
+        caches.append((kc, vc))
+    q = bits_to_bf16(w.q).to(dev)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    cu = torch.from_numpy(cu_np).to(dev)
+    out = torch.empty((n, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        kc, vc = caches[i % copies]
+        pkv.paged_prefill(q, kc, vc, bt, lens, cu, w.block_size, w.scale, out,
+                          max_q_len=int(ql.max()), max_seq_len=int(w.seq_lens.max()))
+
+    trials = [timed(stream, step, args.steps, args.warmup) for _ in range(max(1, args.trials))]
+    ms = float(np.median(trials))
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "workload": "prefill_chunked", "metric": "paged prefill attention matrix-core rate",
+        "us_per_step": round(ms * 1e3, 3), "new_tokens": n,
+        "new_tokens_per_s": round(n / (ms * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "algorithmic_flops_per_launch": flops,
+                     "note": "4 D flops per (new token, q head, visible position)"},
+        "kv_bytes_cached": w.kv_bytes(), "cache_copies_rotated": copies,
+        "trials_us": [round(t * 1e3, 3) for t in trials], "steps": args.steps}), flush=True)
+    return 0
+
+
 def run_pool16(args) -> int:
     """The 16-layer decode step at pool scale: 2^22 slots per layer (8 GiB of
     K+V per layer), 256 sequences with lognormal lengths (median 1200, capped
@@ -416,6 +483,8 @@ def main() -> int:
         return run_prefix_cow(args)
     if args.workload == "pool16":
         return run_pool16(args)
+    if args.workload == "prefill_chunked":
+        return run_prefill(args)
 
     import torch
 

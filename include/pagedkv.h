@@ -309,6 +309,37 @@ pkv_status pkv_cascade_decode(const void* q, const void* k_cache, const void* v_
                               float scale, void* out, const pkv_decode_dims* dims,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* Paged prefill: causal multi-query attention of each sequence's new tokens
+ * over its cached tokens, read through the block table [PU §KV Cache 为什么会
+ * 浪费显存: prefill processes the prompt and builds the cache, and in causal
+ * attention a token attends to the tokens before it; PU §Continuous Batching:
+ * paging (and FlashAttention) keep the dense attention semantics; PU §按 Block
+ * 分配: position t is read through logical block t / B, offset t % B].
+ *   q           bf16 [num_tokens, Hq, D]: the new tokens' queries, sequence by
+ *               sequence.
+ *   cu_q_lens   device int32 [S + 1]: sequence b's new tokens are rows
+ *               cu_q_lens[b] .. cu_q_lens[b+1]-1 of q and out; 0 = cu_q_lens[0]
+ *               <= ... <= cu_q_lens[S] = num_tokens.
+ *   seq_lens    T_b: every cached token of sequence b, its q_len_b new ones
+ *               included (their K,V written first, e.g. by
+ *               pkv_reshape_and_cache); q_len_b <= T_b.
+ *   max_q_len   host bound on q_len_b (sizes the grid; a longer chunk is still
+ *               computed, only more slowly); <= dims->max_seq_len.
+ *   out         [num_tokens, Hq, D] in dims->out_dtype.
+ * New token i of sequence b sits at position T_b - q_len_b + i and attends the
+ * positions 0 .. its own; query head h reads KV head h / G.  dims as for
+ * pkv_paged_attention_decode (kernel, partition and stream fields ignored);
+ * head_dim 64 or 128, block_size 8, 16 or 32, group <= 16.  No workspace.
+ * A sequence whose row range is not inside [0, num_tokens) is skipped; one
+ * with q_len_b > T_b or T_b above the table's capacity gets NaN rows.
+ * q, k_cache and v_cache 16-byte aligned.
+ * Returns PKV_OK, or an error status with nothing enqueued. */
+pkv_status pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             const int32_t* cu_q_lens, int32_t num_tokens, int32_t max_q_len,
+                             int32_t block_size, float scale, void* out,
+                             const pkv_decode_dims* dims, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int32_t status);
 

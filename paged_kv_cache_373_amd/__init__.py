@@ -21,7 +21,7 @@ from .block_manager import BlockManager, PoolExhaustedError, slot_mapping_for
 
 __all__ = [
     "lib", "paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
-    "copy_blocks", "cascade_decode", "cascade_workspace_size",
+    "copy_blocks", "cascade_decode", "cascade_workspace_size", "paged_prefill",
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
     "BlockManager",
     "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
         L.pkv_cascade_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                          ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.pkv_cascade_decode.restype = ctypes.c_int
+        L.pkv_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float,
+                                        vp, dims_p, vp]
+        L.pkv_paged_prefill.restype = ctypes.c_int
         L.pkv_read_probe.argtypes = [vp, vp, i64, vp, vp]
         L.pkv_read_probe.restype = ctypes.c_int
         L.pkv_status_string.argtypes = [i32]
@@ -394,6 +397,44 @@ def cascade_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                               _stream(stream))
     if st != PKV_OK:
         raise PagedKVError(st, "pkv_cascade_decode")
+    return out
+
+
+def paged_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_tables: torch.Tensor, seq_lens: torch.Tensor, cu_q_lens: torch.Tensor,
+                  block_size: int, scale: float, out: torch.Tensor, *, max_q_len: int,
+                  max_seq_len: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Causal multi-query attention of each sequence's new tokens over its
+    cached tokens ([PU §KV Cache 为什么会浪费显存]; [PU §Continuous Batching];
+    [PU §按 Block 分配]).  ``q``/``out`` [N, Hq, D] hold the new tokens
+    sequence by sequence (rows cu_q_lens[b] .. cu_q_lens[b+1]-1, int32 [S+1]
+    on the device); they are the last q_len_b of the seq_lens[b] cached
+    tokens, whose K/V are already in the cache."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(v_cache, "v_cache", torch.bfloat16, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(seq_lens, "seq_lens", torch.int32, 1)
+    _check(cu_q_lens, "cu_q_lens", torch.int32, 1)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, "out", out.dtype, 3)
+    n, hq, d = q.shape
+    p, hkv, bs, d2 = k_cache.shape
+    s = seq_lens.shape[0]
+    if bs != block_size or d2 != d or tuple(v_cache.shape) != (p, hkv, d, bs):
+        raise ValueError("cache shapes must be k [P,Hkv,B,D] and v [P,Hkv,D,B] matching q")
+    if tuple(out.shape) != (n, hq, d) or block_tables.shape[0] != s or cu_q_lens.shape[0] != s + 1:
+        raise ValueError("q, out, block_tables, seq_lens and cu_q_lens disagree")
+    mb = block_tables.shape[1]
+    dims = DecodeDims(s, hq, hkv, d, p, mb, mb * bs if max_seq_len is None else int(max_seq_len),
+                      0, _DTYPES[out.dtype], 0, 0, 0, 0)
+    st = lib().pkv_paged_prefill(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 block_tables.data_ptr(), seq_lens.data_ptr(),
+                                 cu_q_lens.data_ptr(), n, int(max_q_len), bs, float(scale),
+                                 out.data_ptr(), ctypes.byref(dims), _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_paged_prefill")
     return out
 
 

@@ -532,3 +532,53 @@ pkv_status pkv_cascade_decode(const void* q, const void* k_cache, const void* v_
 }
 
 }  // extern "C"
+
+extern "C" {
+
+pkv_status pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             const int32_t* cu_q_lens, int32_t num_tokens, int32_t max_q_len,
+                             int32_t block_size, float scale, void* out,
+                             const pkv_decode_dims* d, void* stream) {
+  if (d == nullptr) return PKV_ERR_INVALID;
+  if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 ||
+      block_size < 1 || d->num_blocks < 1 || d->max_blocks_per_seq < 1 || d->max_seq_len < 0 ||
+      num_tokens < 0 || max_q_len < 0 || max_q_len > d->max_seq_len)
+    return PKV_ERR_INVALID;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(d->max_seq_len) >
+      static_cast<int64_t>(d->max_blocks_per_seq) * block_size)
+    return PKV_ERR_INVALID;
+  if (d->out_dtype != PKV_DTYPE_BF16 && d->out_dtype != PKV_DTYPE_F32) return PKV_ERR_INVALID;
+  const int32_t group = d->num_q_heads / d->num_kv_heads;
+  if (!pkv::prefill_shape_supported(d->head_dim, block_size, group) ||
+      d->num_seqs > kMaxGridYZ || d->num_kv_heads > kMaxGridYZ)
+    return PKV_ERR_UNSUPPORTED;
+  if (d->num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return PKV_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
+      seq_lens == nullptr || cu_q_lens == nullptr || out == nullptr)
+    return PKV_ERR_INVALID;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
+  pkv::PrefillLaunch a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.num_seqs = d->num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = d->num_q_heads;
+  a.num_kv_heads = d->num_kv_heads;
+  a.group = group;
+  a.head_dim = d->head_dim;
+  a.block_size = block_size;
+  a.max_blocks_per_seq = d->max_blocks_per_seq;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+  a.out_f32 = d->out_dtype == PKV_DTYPE_F32 ? 1 : 0;
+  a.out = out;
+  return hip_status(pkv::launch_prefill(a, max_q_len, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

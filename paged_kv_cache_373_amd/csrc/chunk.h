@@ -198,8 +198,14 @@ struct Mfma {
   // (valid in 1..32, wave-uniform) lie past the sequence: their scores are
   // selected to -inf and their V rows to 0, so whatever those slots hold
   // (NaN included) never reaches the result.
+  //
+  // With kCausal, `lim` (per lane) is how many of the chunk's tokens the
+  // lane's row r may see (causal attention: a row sees the positions up to its
+  // own); the later ones get -inf scores as well.  The V rows are masked by
+  // `valid` alone.
+  template <bool kCausal = false>
   static __device__ void step(const bf16x8_t (&qop)[HS], Regs& x, int valid, float sl, int c,
-                              State& st) {
+                              State& st, int lim = 32) {
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hs = 0; hs < HS; ++hs) {
@@ -215,7 +221,11 @@ struct Mfma {
     }
     const bool tail = valid < 32;   // wave-uniform
     const int lv = valid - 8 * c;   // tokens of this lane group still in range
-    if (tail) {
+    if constexpr (kCausal) {
+      const int lvc = min(valid, lim) - 8 * c;  // and visible to this lane's row
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[e] = (e < lvc) ? xs[e] : -INFINITY;
+    } else if (tail) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xs[e] = (e < lv) ? xs[e] : -INFINITY;
     }

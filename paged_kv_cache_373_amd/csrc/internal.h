@@ -151,4 +151,23 @@ struct CascadeLaunch {
 bool cascade_shape_supported(int head_dim, int block_size, int group, int num_seqs);
 hipError_t launch_cascade(const CascadeLaunch& a, hipStream_t stream);
 
+// Paged prefill (causal multi-query attention).  The new tokens of sequence
+// b are rows cu_q_lens[b] .. cu_q_lens[b+1]-1 of q and out, the last q_len_b
+// of its seq_lens[b] cached tokens.
+struct PrefillLaunch {
+  const uint16_t* q;           // bf16 [num_tokens, Hq, D]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;     // [S]
+  const int32_t* cu_q_lens;    // [S + 1]
+  int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, group, head_dim, block_size;
+  int32_t max_blocks_per_seq;
+  float scale_log2;
+  int32_t out_f32;
+  void* out;                   // [num_tokens, Hq, D]
+};
+bool prefill_shape_supported(int head_dim, int block_size, int group);
+hipError_t launch_prefill(const PrefillLaunch& a, int max_q_len, hipStream_t stream);
+
 }  // namespace pkv

@@ -1,0 +1,197 @@
+// prefill.hip - paged prefill (causal multi-query) attention for gfx950.
+//
+// Sources (by title and section):
+//   [PU] Fanyi Pu, "Infra: PagedAttention":
+//        section "KV Cache 为什么会浪费显存": prefill processes the prompt and
+//        builds the cache; in causal attention a token attends to the tokens
+//        before it, whose K,V the cache keeps.
+//        section "Continuous Batching": paging and FlashAttention both keep the
+//        dense attention semantics; the attention reads the paged layout.
+//        section "按 Block 分配": position t lives in logical block t / B at
+//        offset t % B, found through the block table.
+//
+// The new tokens of sequence b are the last q_len_b of its T_b cached tokens
+// (their K,V already written, e.g. by reshape_and_cache); new token i sits at
+// position ctx_b + i, ctx_b = T_b - q_len_b, and attends positions 0 .. its own.
+//
+// Work: a wavefront folds one tile of 16 query rows of one (sequence, KV head)
+// - row R = i G + g is new token i's query head g of the KV head - over the
+// 32-token chunks up to the tile's last position, with the chunk step of the
+// decode kernels (scores and P.V on the matrix cores, online softmax) plus a
+// per-row causal limit.  The tiles of a (sequence, KV head) run latest first,
+// so the longest causal ranges start first; the four wavefronts of a
+// workgroup take neighbouring tiles, which read the same chunks.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "chunk.h"
+#include "internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kNW = 4;  // wavefronts per workgroup
+
+template <int D, int BS>
+__global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
+    prefill_mfma(const PrefillLaunch a) {
+  using M = Mfma<D, BS>;
+  using Regs = typename M::Regs;
+  constexpr int NB = M::NB;
+  constexpr int HS = M::HS;
+  constexpr int NT = M::NT;
+  constexpr int DEPTH = kDepth;
+  static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
+  constexpr int kBatchChunks = 64 / NB;  // chunks whose blocks one batch of lane loads covers
+
+  const int b = blockIdx.z;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int c = lane >> 4;
+  const int r = lane & 15;
+  const int G = a.group;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+
+  // The sequence's rows in q/out and its lengths.  A row range outside
+  // [0, num_tokens) is skipped; q_len > T (or T beyond the table) makes the
+  // sequence's rows NaN.
+  const int q0 = a.cu_q_lens[b];
+  const int q1 = a.cu_q_lens[b + 1];
+  if (q0 < 0 || q1 < q0 || q1 > a.num_tokens) return;
+  const int nq = q1 - q0;
+  const int T = a.seq_lens[b];
+  const int ntiles = (nq * G + 15) / 16;
+  const int wave0 = blockIdx.x * kNW + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * kNW;
+  if (nq > T || T > a.max_blocks_per_seq * BS) {
+    for (int e = wave0 * 64 + lane; e < nq * G * D; e += nwaves * 64) {
+      const int row = e / (G * D);
+      const int rem = e - row * G * D;
+      store_out(a.out, (static_cast<size_t>(q0 + row) * Hq + h * G) * D + rem, NAN, a.out_f32);
+    }
+    return;
+  }
+  const int ctx = T - nq;
+  const float sl = a.scale_log2;
+  const size_t blk_stride = static_cast<size_t>(Hkv) * M::kTile;
+  const size_t head_off = static_cast<size_t>(h) * M::kTile;
+  const int32_t* row_bt = a.block_tables + static_cast<size_t>(b) * a.max_blocks_per_seq;
+  const typename M::Lane ln(c, r);
+  struct Slot {
+    Regs x;
+  };
+
+  for (int j = wave0; j < ntiles; j += nwaves) {
+    const int tile = ntiles - 1 - j;  // latest tiles first
+    // This lane's row (r) of the tile: new token i, head g; past nq the row is
+    // a zero query whose output is dropped.
+    const int R = tile * 16 + r;
+    const int i = R / G;
+    const int g = R - i * G;
+    const bool live = i < nq;
+    const int last_i = min(nq - 1, (tile * 16 + 15) / G);
+    const int pos_max = ctx + last_i;      // the tile's last position
+    const int pos = live ? ctx + i : pos_max;
+    const int nk = pos_max / 32 + 1;       // chunks up to the tile's last position
+    const int last_blk = (min(T, 32 * nk) - 1) / BS;
+    bf16x8_t qop[HS];
+    {
+      const uint16_t* qrow =
+          a.q + (static_cast<size_t>(q0 + (live ? i : 0)) * Hq + h * G + (live ? g : 0)) * D + 8 * c;
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) qop[hs] = live ? load_bf16x8(qrow + 32 * hs) : bf16x8_t{};
+    }
+    typename M::State st;
+    st.reset();
+
+    for (int k0 = 0; k0 < nk; k0 += kBatchChunks) {
+      // the batch's blocks, one per lane (clamped to the last one needed)
+      const int first_blk = k0 * NB;
+      const int bid = row_bt[min(first_blk + lane, last_blk)];
+      const int nkb = min(kBatchChunks, nk - k0);
+      auto issue = [&](int kb, Slot& sl8) {
+        size_t base[NB];
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb)
+          base[jb] = static_cast<size_t>(__builtin_amdgcn_readlane(
+                         bid, min(kb * NB + jb, last_blk - first_blk))) *
+                         blk_stride +
+                     head_off;
+        M::load(a.k_cache, a.v_cache, base, ln, sl8.x);
+      };
+      auto consume = [&](int kb, Slot& sl8) {
+        const int t0 = 32 * (k0 + kb);
+        M::template step<true>(qop, sl8.x, min(32, T - t0), sl, c, st, pos - t0 + 1);
+      };
+      // every refill issues its loads (one past the batch re-reads its last
+      // chunk, which is not folded again) so the wait counts stay exact
+      Slot ring[DEPTH];
+#pragma unroll
+      for (int s = 0; s < DEPTH; ++s) issue(min(s, nkb - 1), ring[s]);
+      for (int kb = 0;;) {
+        if (kb >= nkb) break;
+        consume(kb, ring[0]);
+        issue(min(kb + DEPTH, nkb - 1), ring[0]);
+        ++kb;
+        if constexpr (DEPTH > 1) {
+          if (kb >= nkb) break;
+          consume(kb, ring[1]);
+          issue(min(kb + DEPTH, nkb - 1), ring[1]);
+          ++kb;
+        }
+        if constexpr (DEPTH > 2) {
+          if (kb >= nkb) break;
+          consume(kb, ring[2]);
+          issue(min(kb + DEPTH, nkb - 1), ring[2]);
+          ++kb;
+        }
+      }
+    }
+
+    // Lane (c, r) holds row 4 c + e's accumulator for features 16 nt + r and
+    // its sum: the output is their quotient.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int Ro = tile * 16 + 4 * c + e;
+      const int io = Ro / G;
+      if (io < nq) {
+        const int go = Ro - io * G;
+        const float inv = 1.0f / st.lsum[e];
+        const size_t orow = (static_cast<size_t>(q0 + io) * Hq + h * G + go) * D;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          store_out(a.out, orow + 16 * nt + r, st.acc[nt][e] * inv, a.out_f32);
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const PrefillLaunch& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kNW * 64);
+  switch (a.block_size) {
+    case 8: prefill_mfma<D, 8><<<grid, block, 0, stream>>>(a); break;
+    case 16: prefill_mfma<D, 16><<<grid, block, 0, stream>>>(a); break;
+    default: prefill_mfma<D, 32><<<grid, block, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_shape_supported(int head_dim, int block_size, int group) {
+  return (head_dim == 64 || head_dim == 128) &&
+         (block_size == 8 || block_size == 16 || block_size == 32) && group >= 1 && group <= 16;
+}
+
+hipError_t launch_prefill(const PrefillLaunch& a, int max_q_len, hipStream_t stream) {
+  // one wavefront per 16-row tile of the longest sequence's rows (a longer
+  // one is still covered: the wavefronts stride over the tiles)
+  const int tiles = (max_q_len * a.group + 15) / 16;
+  const dim3 grid(static_cast<unsigned>((tiles + kNW - 1) / kNW), a.num_kv_heads, a.num_seqs);
+  return a.head_dim == 64 ? launch_d<64>(a, grid, stream) : launch_d<128>(a, grid, stream);
+}
+
+}  // namespace pkv

@@ -295,3 +295,24 @@ def test_cascade_rejects_before_any_hip_call():
     assert call(ws=ctypes.c_void_p(0x1010)) == pkv.PKV_ERR_WORKSPACE  # not 256-aligned
     assert call(d=_dims(head_dim=80)) == pkv.PKV_ERR_UNSUPPORTED
     assert call(d=_dims(num_seqs=0), ng=0, lp=0) == pkv.PKV_OK  # nothing to do
+
+
+def test_prefill_rejects_before_any_hip_call():
+    lib = pkv.lib()
+    f = ctypes.c_void_p(0x1000)
+
+    def call(q=f, cu=f, n=16, mq=8, d=None, scale=0.125, bs=16):
+        dd = _dims() if d is None else d
+        return lib.pkv_paged_prefill(q, f, f, f, f, cu, n, mq, bs, scale, f, ctypes.byref(dd),
+                                     None)
+    assert call(q=None) == pkv.PKV_ERR_INVALID
+    assert call(cu=None) == pkv.PKV_ERR_INVALID
+    assert call(n=-1) == pkv.PKV_ERR_INVALID
+    assert call(mq=65) == pkv.PKV_ERR_INVALID  # above max_seq_len
+    assert call(scale=float("nan")) == pkv.PKV_ERR_INVALID
+    assert call(q=ctypes.c_void_p(0x1004)) == pkv.PKV_ERR_INVALID
+    assert call(d=_dims(num_q_heads=30)) == pkv.PKV_ERR_INVALID
+    assert call(d=_dims(head_dim=80)) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(bs=4, d=_dims(max_blocks_per_seq=16)) == pkv.PKV_ERR_UNSUPPORTED
+    assert call(n=0) == pkv.PKV_OK  # nothing to do
+    assert call(d=_dims(num_seqs=0)) == pkv.PKV_OK
