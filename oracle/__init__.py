@@ -7,6 +7,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 Sources (cited by title and section):
   [ITH] iThome ithelp article 10405755 on PagedAttention.
   [PU]  Fanyi Pu, "Infra: PagedAttention".
+  [AK]  "只用了 8 格，為什麼占了 12 格？" (the paged-attention story page).
 Everything here is a plain, direct statement of what those pages define:
 
 * :func:`slot` / :func:`num_blocks_for` - where position t lives and how many
@@ -19,6 +20,9 @@ Everything here is a plain, direct statement of what those pages define:
   ([PU §共享前缀，分叉时 Copy-on-write]).
 * :func:`write_cache` / :func:`copy_blocks` - the slot-mapped cache write and
   the whole-block copy, as numpy index assignment on bf16 bit patterns.
+* :func:`swap_out` / :func:`swap_in` - whole blocks out to host memory and
+  back ([AK §故事沒有說完的部分]: pages swapped out under memory pressure and
+  swapped back in; a page may come back anywhere, the table finds it).
 * :func:`merge_states` - the segment merge o = sum_r Z_r o_r / sum_r Z_r
   evaluated with every Z_r rescaled to the common maximum ([PU §按 Block 分配]).
 * :func:`paged_decode` / :func:`dense_decode` - gather K,V into position order
@@ -176,6 +180,30 @@ def copy_blocks(caches: Sequence[np.ndarray], pairs: Sequence[Tuple[int, int]]) 
     for cache in caches:
         for src, dst in pairs:
             cache[dst] = cache[src]
+
+
+def swap_out(caches: Sequence[Tuple[np.ndarray, np.ndarray]],
+             block_ids: Sequence[int]) -> np.ndarray:
+    """Copy whole blocks out to host memory ([AK §故事沒有說完的部分]: when memory
+    runs short some requests' pages are swapped out and later swapped back,
+    which works because a page can live anywhere and is found through the
+    table).  Returns uint16 [L, 2, n, Hkv*B*D]: [l, 0, i] is K block
+    block_ids[i] of layer l and [l, 1, i] its V block, each block's elements in
+    the cache's own order."""
+    ids = np.asarray(block_ids, dtype=np.int64)
+    n = ids.shape[0]
+    return np.stack([np.stack([kc[ids].reshape(n, -1), vc[ids].reshape(n, -1)])
+                     for kc, vc in caches])
+
+
+def swap_in(caches: Sequence[Tuple[np.ndarray, np.ndarray]], block_ids: Sequence[int],
+            buf: np.ndarray) -> None:
+    """The way back: block i of ``buf`` (the layout :func:`swap_out` returns)
+    becomes block ``block_ids[i]`` of every layer's K and V cache."""
+    ids = np.asarray(block_ids, dtype=np.int64)
+    for l, (kc, vc) in enumerate(caches):
+        kc[ids] = buf[l, 0].reshape((ids.shape[0],) + kc.shape[1:])
+        vc[ids] = buf[l, 1].reshape((ids.shape[0],) + vc.shape[1:])
 
 
 def gather(k_cache: np.ndarray, v_cache: np.ndarray, table_row: Sequence[int],

@@ -437,3 +437,47 @@ def test_prefill_first_position_returns_v0_and_future_is_invisible():
     np.testing.assert_array_equal(out2[:cu_q[1] - 1], out[:cu_q[1] - 1])
     np.testing.assert_array_equal(out2[cu_q[1]:], out[cu_q[1]:])
     assert not np.array_equal(out2[cu_q[1] - 1], out[cu_q[1] - 1])
+
+
+# ---------------------------------------------------------------- swap
+
+
+def test_swap_round_trip_and_relocation():
+    """Blocks swapped out and back into the same ids leave every cache bit as
+    it was; swapped back into other ids, with the tables re-pointed there,
+    attention gives the same result bit for bit (the page is found through
+    the table wherever it lives)."""
+    w = workloads.random_small(8, 5, 8, 2, 32, 4, 30, min_len=1, slack_blocks=40)
+    kc, vc = _oracle_cache(w)
+    kc2, vc2 = _oracle_cache(w)
+    caches = [(kc, vc), (kc2, vc2)]
+    before = [(a.copy(), b.copy()) for a, b in caches]
+    used = np.unique(np.concatenate([w.block_tables[b, :-(-int(w.seq_lens[b]) // 4)]
+                                     for b in range(w.num_seqs)]))
+    buf = oracle.swap_out(caches, used[::-1])
+    assert buf.shape == (2, 2, len(used), kc[0].size)
+    np.testing.assert_array_equal(buf[1, 0, 0], kc2[used[-1]].ravel())
+    np.testing.assert_array_equal(buf[0, 1, 2], vc[used[-3]].ravel())
+    ref = oracle.paged_decode(w.q, kc, vc, w.block_tables, w.seq_lens, w.scale)
+    # scribble over the swapped-out blocks, then bring them back where they were
+    for a, b in caches:
+        a[used] = 0x7FC0
+        b[used] = 0x7FC0
+    oracle.swap_in(caches, used[::-1], buf)
+    for (a, b), (a0, b0) in zip(caches, before):
+        np.testing.assert_array_equal(a, a0)
+        np.testing.assert_array_equal(b, b0)
+    # relocate: the blocks come back into free ids, the tables follow them
+    free = np.setdiff1d(np.arange(w.num_blocks), used)[:len(used)]
+    assert len(free) == len(used)
+    moved = dict(zip(used.tolist(), free.tolist()))
+    oracle.swap_in(caches, [moved[int(x)] for x in used[::-1]], buf)
+    bt2 = w.block_tables.copy()
+    for b in range(w.num_seqs):
+        nb = -(-int(w.seq_lens[b]) // 4)
+        bt2[b, :nb] = [moved[int(x)] for x in bt2[b, :nb]]
+    for a, b in caches:  # the old places are gone
+        a[used] = 0x7FC0
+        b[used] = 0x7FC0
+    got = oracle.paged_decode(w.q, kc, vc, bt2, w.seq_lens, w.scale)
+    np.testing.assert_array_equal(got, ref)
