@@ -16,10 +16,10 @@ total) that it cannot sit in the 256 MB Infinity Cache between steps.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
 ``--workload`` is llama_b64 (default, the headline line) or long_splitkv;
-prefix_cow, pool16 and prefill_chunked print their own report lines instead
+prefix_cow, pool16, prefill_chunked and swap print their own report lines instead
 (logical and unique GB/s with the shared-prefix decode and the copy_blocks
 time; the 16-layer pool step per block size; the chunked prefill's matrix-core
-rate).
+rate; block swap-out/in against the host link).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
 GPU.  ``roofline.achieved`` is the decode launch alone (HIP events on the
@@ -375,6 +375,51 @@ def run_prefill(args) -> int:
     return 0
 
 
+def run_swap(args) -> int:
+    """Block swap-out/in of the Llama-shaped pool: 16 layers of 2048 blocks
+    (B = 16, 8 KV heads, head_dim 64: 16 KiB per block per cache), half of
+    the blocks (a seeded random choice) swapped out to pinned host memory and
+    back in.  Reports each direction's rate over the bytes moved, beside a
+    plain contiguous copy of the same size between the device and pinned host
+    memory (the host link's ceiling as the runtime reaches it)."""
+    import torch
+
+    import paged_kv_cache_373_amd as pkv
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    layers, P, hkv, bs, d = 16, 2048, 8, 16, 64
+    n = P // 2
+    kcs, vcs = [], []
+    for _ in range(layers):
+        kc, vc = pkv.new_kv_cache(P, hkv, bs, d, device=dev)
+        kc.normal_()
+        vc.normal_()
+        kcs.append(kc)
+        vcs.append(vc)
+    ids = torch.from_numpy(np.random.default_rng(373).permutation(P)[:n].astype(np.int32)).to(dev)
+    buf = pkv.swap_buffer(kcs, n)
+    nbytes = buf.numel() * buf.element_size()
+    flat = torch.empty(nbytes // 2, dtype=torch.int16, device=dev)
+    flat_host = buf.view(-1)
+
+    steps = max(3, args.steps // 20)
+    ms_out = timed(stream, lambda i: pkv.swap_out(kcs, vcs, ids, buf), steps, 2)
+    ms_in = timed(stream, lambda i: pkv.swap_in(kcs, vcs, ids, buf), steps, 2)
+    ms_d2h = timed(stream, lambda i: flat_host.copy_(flat, non_blocking=True), steps, 2)
+    ms_h2d = timed(stream, lambda i: flat.copy_(flat_host, non_blocking=True), steps, 2)
+    gbs = lambda ms: round(nbytes / (ms * 1e-3) / 1e9, 2)
+    print(json.dumps({
+        "workload": "swap", "layers": layers, "blocks_moved": n, "bytes_moved": nbytes,
+        "swap_out_ms": round(ms_out, 4), "swap_out_gbs": gbs(ms_out),
+        "swap_in_ms": round(ms_in, 4), "swap_in_gbs": gbs(ms_in),
+        "link_ceiling": {"d2h_gbs": gbs(ms_d2h), "h2d_gbs": gbs(ms_h2d),
+                         "kind": "contiguous device <-> pinned host copy of the same bytes"},
+        "swap_out_frac_of_ceiling": round(ms_d2h / ms_out, 4),
+        "swap_in_frac_of_ceiling": round(ms_h2d / ms_in, 4), "steps": steps}), flush=True)
+    return 0
+
+
 def run_pool16(args) -> int:
     """The 16-layer decode step at pool scale: 2^22 slots per layer (8 GiB of
     K+V per layer), 256 sequences with lognormal lengths (median 1200, capped
@@ -485,6 +530,8 @@ def main() -> int:
         return run_pool16(args)
     if args.workload == "prefill_chunked":
         return run_prefill(args)
+    if args.workload == "swap":
+        return run_swap(args)
 
     import torch
 

@@ -249,6 +249,32 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches,
                            int32_t num_layers, const int32_t* block_pairs,
                            int32_t num_pairs, int64_t block_bytes, void* stream);
 
+/* Block swap-out and swap-in [AK §故事沒有說完的部分: when memory runs short,
+ * some requests' pages are swapped out and later swapped back in; this rests
+ * on pages living anywhere and being found through the table, so a block may
+ * come back into a different physical block whose id the table then takes].
+ *   k_caches, v_caches  HOST arrays of num_layers device pointers
+ *                       (1 <= num_layers <= 64), 16-byte aligned.
+ *   block_ids           device int32 [num_ids]: swap-out reads these blocks,
+ *                       swap-in writes them (distinct ids for swap-in).
+ *   block_bytes         bytes per block per cache, a multiple of 16
+ *                       (Hkv * B * D * 2 for the layout above).
+ *   host_buffer         PINNED host memory the device can address (allocated
+ *                       with hipHostMalloc, or torch's pin_memory), 16-byte
+ *                       aligned, holding num_layers * 2 * num_ids * block_bytes
+ *                       bytes laid out [layer][K, V][i]: K block block_ids[i]
+ *                       of layer l at ((2 l) num_ids + i) block_bytes, its V
+ *                       block at ((2 l + 1) num_ids + i) block_bytes.  Pageable
+ *                       memory is refused (PKV_ERR_INVALID).
+ * One launch: the device copies the blocks over the host link itself.
+ * num_ids == 0 enqueues nothing and returns PKV_OK. */
+pkv_status pkv_swap_out(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                        const int32_t* block_ids, int32_t num_ids, int64_t block_bytes,
+                        void* host_buffer, void* stream);
+pkv_status pkv_swap_in(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                       const int32_t* block_ids, int32_t num_ids, int64_t block_bytes,
+                       const void* host_buffer, void* stream);
+
 /* Merge of per-segment attention results [PU §按 Block 分配: with Z_r the sum
  * of e^{s_i} over segment r and o_r that segment's own softmax output,
  * o = sum_r Z_r o_r / sum_r Z_r, evaluated after rescaling every Z_r to the

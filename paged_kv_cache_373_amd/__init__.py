@@ -21,7 +21,8 @@ from .block_manager import BlockManager, PoolExhaustedError, slot_mapping_for
 
 __all__ = [
     "lib", "paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
-    "copy_blocks", "cascade_decode", "cascade_workspace_size", "paged_prefill",
+    "copy_blocks", "cascade_decode", "cascade_workspace_size", "paged_prefill", "swap_out",
+    "swap_in", "swap_buffer",
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
     "BlockManager",
     "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
@@ -99,6 +100,10 @@ def lib() -> ctypes.CDLL:
         L.pkv_paged_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_float,
                                         vp, dims_p, vp]
         L.pkv_paged_prefill.restype = ctypes.c_int
+        for name in ("pkv_swap_out", "pkv_swap_in"):
+            getattr(L, name).argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i64,
+                                         vp, vp]
+            getattr(L, name).restype = ctypes.c_int
         L.pkv_read_probe.argtypes = [vp, vp, i64, vp, vp]
         L.pkv_read_probe.restype = ctypes.c_int
         L.pkv_status_string.argtypes = [i32]
@@ -483,6 +488,53 @@ def copy_blocks(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tenso
                                block_pairs.shape[0], block_bytes, _stream(stream))
     if st != PKV_OK:
         raise PagedKVError(st, "pkv_copy_blocks")
+
+
+def _swap(name, k_caches, v_caches, block_ids, host_buffer, stream):
+    if len(k_caches) != len(v_caches) or not k_caches:
+        raise ValueError("need one k and one v cache per layer")
+    _check(block_ids, "block_ids", torch.int32, 1)
+    shape = tuple(k_caches[0].shape)
+    for kc, vc in zip(k_caches, v_caches):
+        _check(kc, "k_cache", torch.bfloat16, 4)
+        _check(vc, "v_cache", torch.bfloat16, 4)
+        if tuple(kc.shape) != shape or vc.shape[0] != shape[0] or vc.numel() != kc.numel():
+            raise ValueError("all layers must share one cache shape")
+    n_layers, n = len(k_caches), block_ids.shape[0]
+    block_bytes = k_caches[0][0].numel() * 2
+    if host_buffer.is_cuda or not host_buffer.is_pinned() or not host_buffer.is_contiguous():
+        raise ValueError("host_buffer must be a contiguous pinned host tensor")
+    if host_buffer.numel() * host_buffer.element_size() < n_layers * 2 * n * block_bytes:
+        raise ValueError("host_buffer is smaller than layers x 2 x blocks x block bytes")
+    karr = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in k_caches])
+    varr = (ctypes.c_void_p * n_layers)(*[t.data_ptr() for t in v_caches])
+    st = getattr(lib(), name)(karr, varr, n_layers, block_ids.data_ptr(), n, block_bytes,
+                              host_buffer.data_ptr(), _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, name)
+
+
+def swap_buffer(k_caches: Sequence[torch.Tensor], num_ids: int) -> torch.Tensor:
+    """A pinned host buffer for swapping ``num_ids`` blocks of these layers:
+    uint16 [layers, 2, num_ids, Hkv*B*D] (the layout pkv_swap_out writes)."""
+    return torch.empty((len(k_caches), 2, num_ids, k_caches[0][0].numel()), dtype=torch.int16,
+                       pin_memory=True)
+
+
+def swap_out(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor],
+             block_ids: torch.Tensor, host_buffer: torch.Tensor, stream=None) -> None:
+    """Copy blocks ``block_ids`` (int32, on the device) of every layer's K and
+    V cache to the pinned ``host_buffer`` ([AK §故事沒有說完的部分]: pages
+    swapped out under memory pressure).  Asynchronous on the stream."""
+    _swap("pkv_swap_out", k_caches, v_caches, block_ids, host_buffer, stream)
+
+
+def swap_in(k_caches: Sequence[torch.Tensor], v_caches: Sequence[torch.Tensor],
+            block_ids: torch.Tensor, host_buffer: torch.Tensor, stream=None) -> None:
+    """The way back: block i of ``host_buffer`` becomes block block_ids[i] of
+    every layer (which may differ from where it was swapped out from; the
+    table follows it)."""
+    _swap("pkv_swap_in", k_caches, v_caches, block_ids, host_buffer, stream)
 
 
 def merge_attention_states(part_out: torch.Tensor, part_lse: torch.Tensor,

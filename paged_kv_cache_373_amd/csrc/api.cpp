@@ -582,3 +582,52 @@ pkv_status pkv_paged_prefill(const void* q, const void* k_cache, const void* v_c
 }
 
 }  // extern "C"
+
+namespace {
+
+// The swap entry points' checks: the same as copy_blocks for the caches, and
+// the host buffer must be pinned host memory the device can address.
+pkv_status swap_impl(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                     const int32_t* block_ids, int32_t n, int64_t block_bytes, void* host,
+                     int to_host, void* stream) {
+  if (n < 0 || num_layers < 1 || num_layers > pkv::kMaxCopyLayers || block_bytes <= 0 ||
+      block_bytes % 16 != 0)
+    return PKV_ERR_INVALID;
+  if (n == 0) return PKV_OK;
+  if (n > 0x7FFFFFFF / 2 || k_caches == nullptr || v_caches == nullptr || block_ids == nullptr ||
+      host == nullptr || !aligned16(host))
+    return PKV_ERR_INVALID;
+  for (int32_t l = 0; l < num_layers; ++l)
+    if (k_caches[l] == nullptr || v_caches[l] == nullptr || !aligned16(k_caches[l]) ||
+        !aligned16(v_caches[l]))
+      return PKV_ERR_INVALID;
+  hipPointerAttribute_t attr = {};
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the caller's next call
+    return PKV_ERR_INVALID;
+  }
+  if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) return PKV_ERR_INVALID;
+  return hip_status(pkv::launch_swap_blocks(k_caches, v_caches, num_layers, block_ids, n,
+                                            block_bytes, attr.devicePointer, to_host,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_swap_out(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                        const int32_t* block_ids, int32_t num_ids, int64_t block_bytes,
+                        void* host_buffer, void* stream) {
+  return swap_impl(k_caches, v_caches, num_layers, block_ids, num_ids, block_bytes, host_buffer,
+                   1, stream);
+}
+
+pkv_status pkv_swap_in(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                       const int32_t* block_ids, int32_t num_ids, int64_t block_bytes,
+                       const void* host_buffer, void* stream) {
+  return swap_impl(k_caches, v_caches, num_layers, block_ids, num_ids, block_bytes,
+                   const_cast<void*>(host_buffer), 0, stream);
+}
+
+}  // extern "C"

@@ -112,6 +112,36 @@ __global__ void __launch_bounds__(256)
   for (int64_t i = threadIdx.x; i < units_per_block; i += blockDim.x) d[i] = s[i];
 }
 
+// grid (block i, layer, K|V); the workgroup streams one block between the
+// cache and the host buffer (pinned host memory the device reads and writes
+// directly), four 16-byte units per thread in flight at a time.  The host
+// buffer holds [layer][K|V][i] blocks back to back.
+__global__ void __launch_bounds__(256)
+    swap_blocks_kernel(const LayerPtrs ptrs, const int32_t* __restrict__ block_ids, int32_t n,
+                       u32x4_t* host, int64_t units_per_block, int to_host) {
+  const int64_t i = blockIdx.x;
+  const int layer = blockIdx.y;
+  const int z = blockIdx.z;
+  u32x4_t* cache = (z == 0 ? ptrs.k[layer] : ptrs.v[layer]) +
+                   static_cast<int64_t>(block_ids[i]) * units_per_block;
+  u32x4_t* h = host + ((static_cast<int64_t>(layer) * 2 + z) * n + i) * units_per_block;
+  const u32x4_t* src = to_host ? cache : h;
+  u32x4_t* dst = to_host ? h : cache;
+  for (int64_t j0 = threadIdx.x; j0 < units_per_block; j0 += 4 * 256) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t j = j0 + m * 256;
+      if (j < units_per_block) v[m] = src[j];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t j = j0 + m * 256;
+      if (j < units_per_block) dst[j] = v[m];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v,
@@ -151,6 +181,20 @@ hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int3
   }
   const dim3 grid(num_pairs, num_layers, 2);
   copy_blocks_kernel<<<grid, 256, 0, stream>>>(ptrs, block_pairs, block_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                              const int32_t* block_ids, int32_t n, int64_t block_bytes,
+                              void* host_dev, int to_host, hipStream_t stream) {
+  LayerPtrs ptrs = {};
+  for (int l = 0; l < num_layers; ++l) {
+    ptrs.k[l] = static_cast<u32x4_t*>(k_caches[l]);
+    ptrs.v[l] = static_cast<u32x4_t*>(v_caches[l]);
+  }
+  const dim3 grid(static_cast<unsigned>(n), num_layers, 2);
+  swap_blocks_kernel<<<grid, 256, 0, stream>>>(ptrs, block_ids, n, static_cast<u32x4_t*>(host_dev),
+                                                block_bytes / 16, to_host);
   return hipGetLastError();
 }
 

@@ -106,6 +106,12 @@ hipError_t launch_read_probe(const void* src, const int32_t* order, int64_t num_
                              uint32_t* sink, hipStream_t stream);
 
 constexpr int kMaxCopyLayers = 64;
+// Swap: blocks block_ids[0..n) of every layer's K and V cache to (to_host = 1)
+// or from (0) the host buffer, [layer][K|V][i] blocks back to back; host_dev
+// is the buffer's device address.
+hipError_t launch_swap_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
+                              const int32_t* block_ids, int32_t n, int64_t block_bytes,
+                              void* host_dev, int to_host, hipStream_t stream);
 hipError_t launch_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t num_layers,
                               const int32_t* block_pairs, int32_t num_pairs,
                               int64_t block_bytes, hipStream_t stream);

@@ -316,3 +316,24 @@ def test_prefill_rejects_before_any_hip_call():
     assert call(bs=4, d=_dims(max_blocks_per_seq=16)) == pkv.PKV_ERR_UNSUPPORTED
     assert call(n=0) == pkv.PKV_OK  # nothing to do
     assert call(d=_dims(num_seqs=0)) == pkv.PKV_OK
+
+
+def test_swap_rejects_before_any_hip_call():
+    lib = pkv.lib()
+    f = ctypes.c_void_p(0x1000)
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    for name in ("pkv_swap_out", "pkv_swap_in"):
+        fn = getattr(lib, name)
+        fn.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                       ctypes.c_void_p, ctypes.c_void_p]
+        assert fn(arr, arr, 2, f, 0, 4096, f, None) == pkv.PKV_OK  # nothing to move
+        assert fn(arr, arr, 0, f, 4, 4096, f, None) == pkv.PKV_ERR_INVALID
+        assert fn(arr, arr, 65, f, 4, 4096, f, None) == pkv.PKV_ERR_INVALID
+        assert fn(arr, arr, 2, f, -1, 4096, f, None) == pkv.PKV_ERR_INVALID
+        assert fn(arr, arr, 2, f, 4, 4100, f, None) == pkv.PKV_ERR_INVALID  # not whole 16 B
+        assert fn(arr, arr, 2, None, 4, 4096, f, None) == pkv.PKV_ERR_INVALID
+        assert fn(arr, arr, 2, f, 4, 4096, None, None) == pkv.PKV_ERR_INVALID
+        assert fn(arr, arr, 2, f, 4, 4096, ctypes.c_void_p(0x1008), None) == pkv.PKV_ERR_INVALID
+        bad = (ctypes.c_void_p * 2)(0x1000, 0x2004)  # misaligned cache
+        assert fn(bad, arr, 2, f, 4, 4096, f, None) == pkv.PKV_ERR_INVALID
