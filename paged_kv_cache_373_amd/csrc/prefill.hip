@@ -14,13 +14,16 @@
 // (their K,V already written, e.g. by reshape_and_cache); new token i sits at
 // position ctx_b + i, ctx_b = T_b - q_len_b, and attends positions 0 .. its own.
 //
-// Work: a wavefront folds one tile of 16 query rows of one (sequence, KV head)
+// Work: a wavefront folds tiles of 16 query rows of one (sequence, KV head)
 // - row R = i G + g is new token i's query head g of the KV head - over the
-// 32-token chunks up to the tile's last position, with the chunk step of the
+// 32-token chunks up to their last position, with the chunk step of the
 // decode kernels (scores and P.V on the matrix cores, online softmax) plus a
-// per-row causal limit.  The tiles of a (sequence, KV head) run latest first,
-// so the longest causal ranges start first; the four wavefronts of a
-// workgroup take neighbouring tiles, which read the same chunks.
+// per-row causal limit.  It takes three neighbouring tiles at a time at
+// head_dim 64 (one at 128, whose operands take twice the registers): each
+// chunk loaded serves all of them, and their steps interleave.  The tiles of a (sequence, KV head)
+// run latest first, so the longest causal ranges start first; the four
+// wavefronts of a workgroup take neighbouring tiles, which read the same
+// chunks.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -33,6 +36,12 @@ namespace {
 
 constexpr int kNW = 4;  // wavefronts per workgroup
 
+// 16-row tiles a wavefront takes at a time: three at head_dim 64 (measured
+// against one, two and four on the chunked Llama step: 100 us against 180,
+// 113 and 111), one at 128, whose operands and states take twice the
+// registers.
+constexpr int prefill_tiles_per_wave(int head_dim) { return head_dim <= 64 ? 3 : 1; }
+
 template <int D, int BS>
 __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
     prefill_mfma(const PrefillLaunch a) {
@@ -44,6 +53,7 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
   constexpr int DEPTH = kDepth;
   static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
   constexpr int kBatchChunks = 64 / NB;  // chunks whose blocks one batch of lane loads covers
+  constexpr int TPW = prefill_tiles_per_wave(D);
 
   const int b = blockIdx.z;
   const int h = blockIdx.y;
@@ -83,28 +93,37 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
     Regs x;
   };
 
-  for (int j = wave0; j < ntiles; j += nwaves) {
-    const int tile = ntiles - 1 - j;  // latest tiles first
-    // This lane's row (r) of the tile: new token i, head g; past nq the row is
+  // A wavefront takes TPW neighbouring tiles at a time: each chunk it loads
+  // serves all of their rows, and their steps interleave.
+  const int nitems = (ntiles + TPW - 1) / TPW;
+  for (int j = wave0; j < nitems; j += nwaves) {
+    const int tile0 = (nitems - 1 - j) * TPW;  // latest tiles first
+    // This lane's row (r) of tile t: new token i, head g; past nq the row is
     // a zero query whose output is dropped.
-    const int R = tile * 16 + r;
-    const int i = R / G;
-    const int g = R - i * G;
-    const bool live = i < nq;
-    const int last_i = min(nq - 1, (tile * 16 + 15) / G);
-    const int pos_max = ctx + last_i;      // the tile's last position
-    const int pos = live ? ctx + i : pos_max;
-    const int nk = pos_max / 32 + 1;       // chunks up to the tile's last position
-    const int last_blk = (min(T, 32 * nk) - 1) / BS;
-    bf16x8_t qop[HS];
-    {
+    int pos[TPW];
+    bf16x8_t qop[TPW][HS];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int R = (tile0 + t) * 16 + r;
+      const int i = R / G;
+      const int g = R - i * G;
+      const bool live = i < nq;
+      pos[t] = live ? ctx + i : -1;
       const uint16_t* qrow =
           a.q + (static_cast<size_t>(q0 + (live ? i : 0)) * Hq + h * G + (live ? g : 0)) * D + 8 * c;
 #pragma unroll
-      for (int hs = 0; hs < HS; ++hs) qop[hs] = live ? load_bf16x8(qrow + 32 * hs) : bf16x8_t{};
+      for (int hs = 0; hs < HS; ++hs) qop[t][hs] = live ? load_bf16x8(qrow + 32 * hs) : bf16x8_t{};
     }
-    typename M::State st;
-    st.reset();
+    const int last_i = min(nq - 1, ((tile0 + TPW) * 16 - 1) / G);
+    const int pos_max = ctx + last_i;      // the item's last position
+    const int nk = pos_max / 32 + 1;       // chunks up to it
+    const int last_blk = (min(T, 32 * nk) - 1) / BS;
+    // a dead row (past nq) sees every chunk the item reads, so its state stays finite
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) pos[t] = pos[t] < 0 ? pos_max : pos[t];
+    typename M::State st[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) st[t].reset();
 
     for (int k0 = 0; k0 < nk; k0 += kBatchChunks) {
       // the batch's blocks, one per lane (clamped to the last one needed)
@@ -123,7 +142,10 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
       };
       auto consume = [&](int kb, Slot& sl8) {
         const int t0 = 32 * (k0 + kb);
-        M::template step<true>(qop, sl8.x, min(32, T - t0), sl, c, st, pos - t0 + 1);
+        const int valid = min(32, T - t0);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+          M::template step<true>(qop[t], sl8.x, valid, sl, c, st[t], pos[t] - t0 + 1);
       };
       // every refill issues its loads (one past the batch re-reads its last
       // chunk, which is not folded again) so the wait counts stay exact
@@ -150,19 +172,22 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
       }
     }
 
-    // Lane (c, r) holds row 4 c + e's accumulator for features 16 nt + r and
-    // its sum: the output is their quotient.
+    // Lane (c, r) holds row 4 c + e of each tile: its accumulator for
+    // features 16 nt + r and its sum, whose quotient is the output.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int Ro = tile * 16 + 4 * c + e;
-      const int io = Ro / G;
-      if (io < nq) {
-        const int go = Ro - io * G;
-        const float inv = 1.0f / st.lsum[e];
-        const size_t orow = (static_cast<size_t>(q0 + io) * Hq + h * G + go) * D;
+    for (int t = 0; t < TPW; ++t) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          store_out(a.out, orow + 16 * nt + r, st.acc[nt][e] * inv, a.out_f32);
+      for (int e = 0; e < 4; ++e) {
+        const int Ro = (tile0 + t) * 16 + 4 * c + e;
+        const int io = Ro / G;
+        if (io < nq) {
+          const int go = Ro - io * G;
+          const float inv = 1.0f / st[t].lsum[e];
+          const size_t orow = (static_cast<size_t>(q0 + io) * Hq + h * G + go) * D;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            store_out(a.out, orow + 16 * nt + r, st[t].acc[nt][e] * inv, a.out_f32);
+        }
       }
     }
   }
@@ -187,10 +212,13 @@ bool prefill_shape_supported(int head_dim, int block_size, int group) {
 }
 
 hipError_t launch_prefill(const PrefillLaunch& a, int max_q_len, hipStream_t stream) {
-  // one wavefront per 16-row tile of the longest sequence's rows (a longer
-  // one is still covered: the wavefronts stride over the tiles)
+  // one wavefront per item (tiles of 16 rows, three per item at head_dim 64) of
+  // the longest sequence's rows (a longer one is still covered: the
+  // wavefronts stride over the items)
   const int tiles = (max_q_len * a.group + 15) / 16;
-  const dim3 grid(static_cast<unsigned>((tiles + kNW - 1) / kNW), a.num_kv_heads, a.num_seqs);
+  const int tpw = prefill_tiles_per_wave(a.head_dim);
+  const int items = (tiles + tpw - 1) / tpw;
+  const dim3 grid(static_cast<unsigned>((items + kNW - 1) / kNW), a.num_kv_heads, a.num_seqs);
   return a.head_dim == 64 ? launch_d<64>(a, grid, stream) : launch_d<128>(a, grid, stream);
 }
 
