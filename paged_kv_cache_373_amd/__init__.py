@@ -17,14 +17,15 @@ from typing import Optional, Sequence
 
 import torch
 
-from .block_manager import BlockManager, PoolExhaustedError, slot_mapping_for
+from .block_manager import BlockManager, PoolExhaustedError, block_key, slot_mapping_for
+from .scheduler import Batcher, Request
 
 __all__ = [
     "lib", "paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
     "copy_blocks", "cascade_decode", "cascade_workspace_size", "paged_prefill", "swap_out",
     "swap_in", "swap_buffer",
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
-    "BlockManager",
+    "BlockManager", "Batcher", "Request", "block_key",
     "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
 ]
 

@@ -16,15 +16,26 @@ says.  The rules are the ones the pages walk through:
   the block, re-points the writer's entry at the copy and then writes.  Full
   prefix blocks are never written again and so stay shared.
 
+* [PU §共享前缀，分叉时 Copy-on-write], the paragraph on Automatic Prefix
+  Caching: requests arriving at different times that start with the same
+  tokens reuse the cached full prefix blocks; the lookup key of a block hashes
+  the previous block's key, the block's tokens and context ids (a LoRA id, for
+  instance), so only a whole matching prefix is reused; only full blocks are
+  cached.  :meth:`BlockManager.add_prompt` does this; a cached block whose
+  last user leaves stays findable until its space is needed.
+
 Pool policy: the free list is a FIFO/LIFO hybrid - blocks are handed out from
 its front and released blocks are put back at its front (most recently freed
-first).  Any free block would be correct; this one is deterministic given the
-initial order.  Running out of blocks raises :class:`PoolExhaustedError`
-without changing any state, so a scheduler can wait and retry.
+first).  Cached blocks nobody uses wait in least-recently-released order and
+are taken (forgetting their key) only when the free list is empty.  Any free
+block would be correct; this policy is deterministic given the initial order.
+Running out of blocks raises :class:`PoolExhaustedError` without changing any
+state, so a scheduler can wait and retry.
 """
 from __future__ import annotations
 
-from collections import deque
+import hashlib
+from collections import OrderedDict, deque
 from typing import Dict, Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -48,6 +59,17 @@ def slot_mapping_for(block_tables: np.ndarray, seq_ids: np.ndarray, positions: n
     return out
 
 
+def block_key(prev: Optional[bytes], tokens: Sequence[int], extra: Sequence = ()) -> bytes:
+    """Lookup key of a full block: sha256 over the previous block's key (32
+    zero bytes for the first block), the block's token ids (int64, little
+    endian) and the context ids ``extra``."""
+    h = hashlib.sha256()
+    h.update(prev if prev is not None else bytes(32))
+    h.update(np.asarray(list(tokens), dtype="<i8").tobytes())
+    h.update(repr(tuple(extra)).encode())
+    return h.digest()
+
+
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int,
                  free_order: Optional[Iterable[int]] = None):
@@ -62,11 +84,27 @@ class BlockManager:
         self.refcount = np.zeros(self.num_blocks, dtype=np.int32)
         self._tables: Dict[object, List[int]] = {}
         self._lengths: Dict[object, int] = {}
+        # prefix caching: key <-> block for cached full blocks, cached blocks
+        # nobody uses (least recently released first), and per sequence the
+        # key of its last full block, its tail tokens and context ids
+        self._index: Dict[bytes, int] = {}
+        self._key_of: Dict[int, bytes] = {}
+        self._idle: "OrderedDict[int, None]" = OrderedDict()
+        self._chain: Dict[object, Tuple[Optional[bytes], List[int], tuple]] = {}
 
     # -- queries -------------------------------------------------------------
     @property
     def num_free(self) -> int:
-        return len(self._free)
+        """Blocks that can be handed out: free ones and cached ones nobody uses."""
+        return len(self._free) + len(self._idle)
+
+    @property
+    def num_cached(self) -> int:
+        """Full blocks findable by key (in use or not)."""
+        return len(self._index)
+
+    def has_sequence(self, seq) -> bool:
+        return seq in self._tables
 
     def table(self, seq) -> List[int]:
         return list(self._tables[seq])
@@ -124,11 +162,73 @@ class BlockManager:
 
     # -- mutations -----------------------------------------------------------
     def _pop(self, n: int = 1) -> List[int]:
-        if n > len(self._free):
-            raise PoolExhaustedError(f"need {n} blocks, {len(self._free)} free")
-        blocks = [self._free.popleft() for _ in range(n)]
+        if n > self.num_free:
+            raise PoolExhaustedError(f"need {n} blocks, {self.num_free} free")
+        blocks = []
+        for _ in range(n):
+            if self._free:
+                blocks.append(self._free.popleft())
+            else:  # the least recently released cached block loses its key
+                blk, _ = self._idle.popitem(last=False)
+                del self._index[self._key_of.pop(blk)]
+                blocks.append(blk)
         self.refcount[blocks] = 1
         return blocks
+
+    def _extend_chain(self, seq, new_tokens: Sequence[int]) -> None:
+        """``seq`` has just grown by ``new_tokens`` (its length already counts
+        them): every block they fill gets its key, chained from the previous
+        block's, unless that key or that block is already keyed."""
+        prev, tail, extra = self._chain[seq]
+        tail = tail + list(new_tokens)
+        table, bs = self._tables[seq], self.block_size
+        start = self._lengths[seq] - len(tail)  # a block boundary
+        while len(tail) >= bs:
+            key = block_key(prev, tail[:bs], extra)
+            blk = table[start // bs]
+            if key not in self._index and blk not in self._key_of:
+                self._index[key] = blk
+                self._key_of[blk] = key
+            prev, tail, start = key, tail[bs:], start + bs
+        self._chain[seq] = (prev, tail, extra)
+
+    def add_prompt(self, seq, token_ids: Sequence[int],
+                   extra: Sequence = ()) -> Tuple[np.ndarray, int]:
+        """Start ``seq`` with the prompt ``token_ids``, reusing cached full
+        blocks for its longest prefix whose keys (chained from the first
+        block, with context ids ``extra``) are known.  Returns the slots of
+        the positions after that prefix, which the caller writes, and the
+        number of cached tokens (a multiple of B) whose K/V are already there.
+        The prompt's new full blocks become findable at once: the caller
+        writes them before another request can read them.  Later tokens keep
+        the chain going when :meth:`append_tokens` is given their ids.
+        All-or-nothing on pool exhaustion."""
+        if seq in self._tables:
+            raise KeyError(f"sequence {seq!r} exists")
+        toks, bs, extra = [int(t) for t in token_ids], self.block_size, tuple(extra)
+        hits, prev = [], None
+        for j in range(len(toks) // bs):
+            key = block_key(prev, toks[j * bs:(j + 1) * bs], extra)
+            blk = self._index.get(key)
+            if blk is None:
+                break
+            hits.append(blk)
+            prev = key
+        need = -(-len(toks) // bs) - len(hits)
+        available = self.num_free - sum(1 for b in hits if b in self._idle)
+        if need > available:
+            raise PoolExhaustedError(f"need {need} blocks, {available} free")
+        for blk in hits:
+            self._idle.pop(blk, None)
+            self.refcount[blk] += 1
+        cached = len(hits) * bs
+        self._tables[seq] = hits + self._pop(need)
+        self._lengths[seq] = len(toks)
+        self._chain[seq] = (prev, [], extra)
+        self._extend_chain(seq, toks[cached:])
+        pos = np.arange(cached, len(toks), dtype=np.int64)
+        blk = np.asarray(self._tables[seq], dtype=np.int64)[pos // bs]
+        return blk * bs + pos % bs, cached
 
     def add_sequence(self, seq) -> None:
         if seq in self._tables:
@@ -136,10 +236,17 @@ class BlockManager:
         self._tables[seq] = []
         self._lengths[seq] = 0
 
-    def append_tokens(self, seq, count: int) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+    def append_tokens(self, seq, count: int,
+                      token_ids: Optional[Sequence[int]] = None
+                      ) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
         """Reserve the next ``count`` positions of ``seq``.  Returns their
         slots (int64) and the (src, dst) block copies that must run before
-        anything is written.  All-or-nothing on pool exhaustion."""
+        anything is written.  For a sequence started by :meth:`add_prompt`,
+        ``token_ids`` (the tokens placed there) keep its blocks findable as
+        they fill; without them its later blocks are not cached.
+        All-or-nothing on pool exhaustion."""
+        if token_ids is not None and len(token_ids) != count:
+            raise ValueError("token_ids must hold count ids")
         table = self._tables[seq]
         start = self._lengths[seq]
         bs = self.block_size
@@ -150,9 +257,9 @@ class BlockManager:
         have = len(table)
         need_new = -(-end // bs) - have
         tail_shared = start % bs != 0 and self.refcount[table[start // bs]] > 1
-        if need_new + int(tail_shared) > len(self._free):
+        if need_new + int(tail_shared) > self.num_free:
             raise PoolExhaustedError(
-                f"need {need_new + int(tail_shared)} blocks, {len(self._free)} free")
+                f"need {need_new + int(tail_shared)} blocks, {self.num_free} free")
         if tail_shared:
             old = table[start // bs]
             (new,) = self._pop(1)
@@ -162,6 +269,11 @@ class BlockManager:
         if need_new > 0:
             table.extend(self._pop(need_new))
         self._lengths[seq] = end
+        if seq in self._chain:
+            if token_ids is None:
+                del self._chain[seq]
+            else:
+                self._extend_chain(seq, [int(t) for t in token_ids])
         pos = np.arange(start, end, dtype=np.int64)
         blk = np.asarray(table, dtype=np.int64)[pos // bs]
         return blk * bs + pos % bs, copies
@@ -178,16 +290,25 @@ class BlockManager:
         table = list(self._tables[parent])
         self._tables[child] = table
         self._lengths[child] = self._lengths[parent]
+        if parent in self._chain:
+            prev, tail, extra = self._chain[parent]
+            self._chain[child] = (prev, list(tail), extra)
         np.add.at(self.refcount, np.asarray(table, dtype=np.int64), 1)
 
     def release(self, seq) -> List[int]:
-        """Drop ``seq``; returns the blocks that became free."""
+        """Drop ``seq``; returns the blocks nobody uses any more.  A cached
+        full block among them stays findable (and is handed out again only
+        when the free list runs dry); the others go back to the free list."""
         table = self._tables.pop(seq)
         del self._lengths[seq]
+        self._chain.pop(seq, None)
         freed = []
         for blk in table:
             self.refcount[blk] -= 1
             if self.refcount[blk] == 0:
-                self._free.appendleft(blk)
+                if blk in self._key_of:
+                    self._idle[blk] = None
+                else:
+                    self._free.appendleft(blk)
                 freed.append(blk)
         return freed
