@@ -304,6 +304,10 @@ def run_prefix_cow(args) -> int:
         "cascade_logical_gbs": round(logical / (ms_casc * 1e-3) / 1e9, 1),
         "cascade_unique_gbs": round(unique / (ms_casc * 1e-3) / 1e9, 1),
         "cascade_groups": int(len(pl_np)), "cascade_prefix_tokens": int(pl_np.max()),
+        "cascade_roofline": {"bound": "hbm", "achieved": round(unique / (ms_casc * 1e-3) / 1e9, 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(unique / (ms_casc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "note": "unique K/V bytes (each block once) per call of both launches"},
         "copy_blocks_pairs": len(pairs), "copy_blocks_bytes": 2 * len(pairs) * hkv * bs * d * 2,
         "copy_blocks_us": round(ms_cow * 1e3, 3), "cache_copies_rotated": copies,
         "blocks_in_use": len(used), "steps": args.steps}), flush=True)
