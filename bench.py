@@ -579,7 +579,9 @@ def main() -> int:
     q = bits_to_bf16(w.q).to(dev)
     out = torch.empty((s, hq, d), dtype=torch.bfloat16, device=dev)
     max_len = int(w.seq_lens.max())
-    ps = args.partition_size or w.partition_size
+    # the library chooses the split (the partitioned kernel with the
+    # workload's own segment length is a parity case: --partition-size 512)
+    ps = args.partition_size
     workspace = pkv.DecodeWorkspace(device=dev)
     stream = torch.cuda.current_stream()
 
