@@ -665,6 +665,14 @@ def main() -> int:
                               else "paged_attention_decode_append (write + attention fused)"),
             "hbm_peak_frac_of_step": round(value / HBM_PEAK_GBS, 4),
             "tokens_per_s_per_layer_step": round(s / (ms_step * 1e-3), 1),
+            # the step's other algorithmic bytes besides the K/V (the counters'
+            # measured total is roofline.traffic): queries, outputs, the table
+            # entries read, sequence lengths and the new tokens' rows written
+            "other_bytes_per_step": {
+                "q": s * hq * d * 2, "out_bf16": s * hq * d * 2,
+                "table_entries": int(sum(-(-int(t) // bs) for t in w.seq_lens)) * 4,
+                "seq_lens": s * 4,
+                "new_token_rows_written": 0 if args.unfused else s * hkv * d * 2 * 2},
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
