@@ -116,6 +116,7 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
     }
     const int last_i = min(nq - 1, ((tile0 + TPW) * 16 - 1) / G);
     const int pos_max = ctx + last_i;      // the item's last position
+    const int pos_min = ctx + (tile0 * 16) / G;  // and its first (every row sees up to here)
     const int nk = pos_max / 32 + 1;       // chunks up to it
     const int last_blk = (min(T, 32 * nk) - 1) / BS;
     // a dead row (past nq) sees every chunk the item reads, so its state stays finite
@@ -142,10 +143,16 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
       };
       auto consume = [&](int kb, Slot& sl8) {
         const int t0 = 32 * (k0 + kb);
-        const int valid = min(32, T - t0);
+        if (pos_min - t0 >= 31) {
+          // every row of the item sees the whole chunk: no mask to apply
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
-          M::template step<true>(qop[t], sl8.x, valid, sl, c, st[t], pos[t] - t0 + 1);
+          for (int t = 0; t < TPW; ++t) M::step(qop[t], sl8.x, 32, sl, c, st[t]);
+        } else {
+          const int valid = min(32, T - t0);
+#pragma unroll
+          for (int t = 0; t < TPW; ++t)
+            M::template step<true>(qop[t], sl8.x, valid, sl, c, st[t], pos[t] - t0 + 1);
+        }
       };
       // every refill issues its loads (one past the batch re-reads its last
       // chunk, which is not folded again) so the wait counts stay exact
