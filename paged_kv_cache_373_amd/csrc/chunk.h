@@ -49,6 +49,19 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum over the four 16-lane rows of the wavefront at each lane's column
+// (lanes r, 16 + r, 32 + r and 48 + r), on every lane.  The two row-swap
+// instructions of gfx950 pair rows (0,1) and (2,3), then halves (0,1) and
+// (2,3), in registers: no trip through the LDS crossbar as a shuffle takes.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float t = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const uint32_t w = __float_as_uint(t);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
 // Device-coherent accesses for data that workgroups hand to each other inside
 // one launch (split-KV partials): atomic at agent scope, so each access is
 // coherent across the chip's L2 caches by itself and no cache-wide write-back
@@ -232,8 +245,7 @@ struct Mfma {
     float cm = xs[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) cm = fmaxf(cm, xs[e]);
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    cm = max_over_rows(cm);
     // every lane of head g now holds the chunk maximum of head g
     if (__ballot(cm > st.m2 + kRescaleThreshold) != 0) {
       const float mn = fmaxf(st.m2, cm);
