@@ -171,7 +171,8 @@ int32_t pkv_decode_plan_kernel(const pkv_decode_dims* dims, int32_t block_size);
  *   seq_lens     int32 [S]; T_b = number of cached tokens of sequence b,
  *                including the token being decoded (whose K/V must already be
  *                in the cache).  0 <= T_b <= dims->max_seq_len.
- *   block_size   B >= 1.   scale  multiplier of q.k (normally 1/sqrt(D)).
+ *   block_size   B >= 1.   scale  multiplier of q.k (normally 1/sqrt(D)), finite and > 0
+ *                (PKV_ERR_INVALID otherwise; every call taking a scale).
  *   out          [S, Hq, D] contiguous, dims->out_dtype.  Query head h reads
  *                KV head h / G (consecutive query heads share a KV head).
  *                A sequence with T_b == 0 gets an all-zero row.

@@ -256,7 +256,7 @@ pkv_status decode_impl(const void* q, const void* k_new, const void* v_new, cons
                  !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
                  !aligned16(v_cache)))
     return PKV_ERR_INVALID;
-  if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PKV_ERR_INVALID;  // the kernels need scale > 0
   if (p.family != kGeneric && (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)))
     return PKV_ERR_INVALID;
   if (p.workspace_bytes > 0) {
@@ -494,7 +494,7 @@ pkv_status pkv_cascade_decode(const void* q, const void* k_cache, const void* v_
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
       seq_lens == nullptr || group_starts == nullptr || prefix_lens == nullptr || out == nullptr)
     return PKV_ERR_INVALID;
-  if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PKV_ERR_INVALID;  // the kernels need scale > 0
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
   if (workspace == nullptr || workspace_bytes < p.workspace_bytes) return PKV_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return PKV_ERR_WORKSPACE;
@@ -558,7 +558,7 @@ pkv_status pkv_paged_prefill(const void* q, const void* k_cache, const void* v_c
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
       seq_lens == nullptr || cu_q_lens == nullptr || out == nullptr)
     return PKV_ERR_INVALID;
-  if (!std::isfinite(scale)) return PKV_ERR_INVALID;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return PKV_ERR_INVALID;  // the kernels need scale > 0
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_ERR_INVALID;
   pkv::PrefillLaunch a = {};
   a.q = static_cast<const uint16_t*>(q);

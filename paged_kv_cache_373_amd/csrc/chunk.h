@@ -49,6 +49,18 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// NaN-propagating maximum (IEEE 754-2019 maximum): one v_maximum3_f32 for up
+// to three operands on gfx950.  Unlike fmaxf it needs no canonicalising of
+// operands the compiler cannot prove canonical (matrix-core results, values
+// moved between lanes), which would cost an instruction per operand.  A NaN
+// operand gives NaN, as it would through the exponential that follows.
+__device__ __forceinline__ float maxnan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float maxnan(float a, float b, float c) {
+  return maxnan(maxnan(a, b), c);
+}
+
 // Maximum over the four 16-lane rows of the wavefront at each lane's column
 // (lanes r, 16 + r, 32 + r and 48 + r), on every lane.  The two row-swap
 // instructions of gfx950 pair rows (0,1) and (2,3), then halves (0,1) and
@@ -56,10 +68,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float max_over_rows(float v) {
   const uint32_t u = __float_as_uint(v);
   const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float t = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  const float t = maxnan(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
   const uint32_t w = __float_as_uint(t);
   const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+  return maxnan(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
 }
 
 // Device-coherent accesses for data that workgroups hand to each other inside
@@ -225,12 +237,13 @@ struct Mfma {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[0][hs], qop[hs], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[1][hs], qop[hs], s1, 0, 0, 0);
     }
-    // xs[e]: score of token 8 c + e in base-2 units, e = 4 u + i
+    // xs[e]: raw score q.k of token 8 c + e, e = 4 u + i (sl > 0 scales it
+    // to base-2 units inside the exponent below, and keeps the order)
     float xs[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xs[i] = s0[i] * sl;
-      xs[4 + i] = s1[i] * sl;
+      xs[i] = s0[i];
+      xs[4 + i] = s1[i];
     }
     const bool tail = valid < 32;   // wave-uniform
     const int lv = valid - 8 * c;   // tokens of this lane group still in range
@@ -242,11 +255,9 @@ struct Mfma {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xs[e] = (e < lv) ? xs[e] : -INFINITY;
     }
-    float cm = xs[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, xs[e]);
-    cm = max_over_rows(cm);
-    // every lane of head g now holds the chunk maximum of head g
+    float cm = maxnan(maxnan(xs[0], xs[1], xs[2]), maxnan(xs[3], xs[4], xs[5]), maxnan(xs[6], xs[7]));
+    cm = max_over_rows(cm) * sl;
+    // every lane of head g now holds the chunk maximum of head g, base-2 units
     if (__ballot(cm > st.m2 + kRescaleThreshold) != 0) {
       const float mn = fmaxf(st.m2, cm);
       const float alpha = fast_exp2(st.m2 - mn);  // 0 on the first chunk (m2 = -inf)
@@ -261,7 +272,7 @@ struct Mfma {
     }
     bf16x8_t pa;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(fast_exp2(xs[e] - st.m2));
+    for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(fast_exp2(fmaf(xs[e], sl, -st.m2)));
     if (tail) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)

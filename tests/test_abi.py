@@ -192,6 +192,10 @@ def test_decode_rejects_before_any_hip_call():
     assert call(q=None) == pkv.PKV_ERR_INVALID
     assert call(out=None) == pkv.PKV_ERR_INVALID
     assert call(scale=float("nan")) == pkv.PKV_ERR_INVALID
+    # the kernels fold the scale into the exponent after the row maximum,
+    # which needs scale > 0
+    assert call(scale=0.0) == pkv.PKV_ERR_INVALID
+    assert call(scale=-0.125) == pkv.PKV_ERR_INVALID
     assert call(q=ctypes.c_void_p(0x1002)) == pkv.PKV_ERR_INVALID  # misaligned for mfma
     bad = _dims(kernel=1, head_dim=48)
     assert call(dims=ctypes.byref(bad)) == pkv.PKV_ERR_UNSUPPORTED
@@ -289,6 +293,8 @@ def test_cascade_rejects_before_any_hip_call():
     assert call(ng=0) == pkv.PKV_ERR_INVALID
     assert call(lp=100) == pkv.PKV_ERR_INVALID
     assert call(scale=float("inf")) == pkv.PKV_ERR_INVALID
+    assert call(scale=0.0) == pkv.PKV_ERR_INVALID
+    assert call(scale=-1.0) == pkv.PKV_ERR_INVALID
     assert call(q=ctypes.c_void_p(0x1002)) == pkv.PKV_ERR_INVALID
     assert call(ws=None) == pkv.PKV_ERR_WORKSPACE
     assert call(wsb=need - 1) == pkv.PKV_ERR_WORKSPACE
@@ -310,6 +316,10 @@ def test_prefill_rejects_before_any_hip_call():
     assert call(n=-1) == pkv.PKV_ERR_INVALID
     assert call(mq=65) == pkv.PKV_ERR_INVALID  # above max_seq_len
     assert call(scale=float("nan")) == pkv.PKV_ERR_INVALID
+    # the kernels fold the scale into the exponent after the row maximum,
+    # which needs scale > 0
+    assert call(scale=0.0) == pkv.PKV_ERR_INVALID
+    assert call(scale=-0.125) == pkv.PKV_ERR_INVALID
     assert call(q=ctypes.c_void_p(0x1004)) == pkv.PKV_ERR_INVALID
     assert call(d=_dims(num_q_heads=30)) == pkv.PKV_ERR_INVALID
     assert call(d=_dims(head_dim=80)) == pkv.PKV_ERR_UNSUPPORTED
