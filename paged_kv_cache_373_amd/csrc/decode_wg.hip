@@ -42,10 +42,12 @@ namespace pkv {
 namespace {
 
 // Words (4 bytes) of LDS per window chunk besides its state: the chunk
-// record (kRecBase + NB words) and a unit record (kUnitWords).
-constexpr int kRecBase = 5;  // sequence, KV head, chunk of unit, valid | flags << 8, unit record
-constexpr int kUnitWords = 3;  // first window position, chunks in window, whole
-constexpr int kMiscWords = 4;  // chunk counter
+// record (kRecBase + NB words), a unit-list entry (kUnitWords) and a merge
+// task (1 word).
+constexpr int kRecBase = 4;    // sequence, KV head, chunk of unit, valid | flags << 8
+constexpr int kUnitWords = 4;  // first window position | chunks << 12 | whole << 24, sequence, head, 0
+constexpr int kMiscWords = 4;  // chunk counter, whole-unit counter, task counter
+constexpr int kBatch = 8;      // slots merged per batch (all their loads in flight at once)
 
 template <int D, int BS, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
@@ -69,7 +71,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   int* s_wsum = lds + lay.off_wsum;
   int* s_misc = lds + lay.off_misc;
   int* s_rec = lds + lay.off_rec;
-  int* s_unit = lds + lay.off_unit;
+  int* s_unit = lds + lay.off_unit;  // unit list: [0] first unit, [1] last unit, [2..] the rest
+  int* s_task = lds + lay.off_task;  // stage-1 merge tasks: first slot | slots << 12
   float* s_acc = reinterpret_cast<float*>(lds + lay.off_acc);  // [capacity][G][16][NT]
   float* s_ml = reinterpret_cast<float*>(lds + lay.off_ml);    // [capacity][G][max, sum]
 
@@ -83,6 +86,13 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int c = lane >> 4;
   const int r = lane & 15;
 
+  // The window's list counters and its last-unit entry start empty (the
+  // prefix's barriers order this before the first window's records).
+  auto clear_lists = [&]() {
+    if (tid < 2) s_misc[1 + tid] = 0;
+    if (tid < kUnitWords) s_unit[kUnitWords + tid] = 0;
+  };
+  clear_lists();
   // 1. Lengths and the chunk prefix; the windows of this workgroup.
   chunk_prefix<NTH>(seq_lens, S, s_len, s_pre, s_wsum, tid);
   const int64_t C = static_cast<int64_t>(Hkv) * s_pre[S];
@@ -128,11 +138,18 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (x >= NWeff) break;
     const int64_t ws = x * C / NWeff;
     const int n = static_cast<int>((x + 1) * C / NWeff - ws);
-    if (k > 0) __syncthreads();  // the previous window's slots are merged
+    if (k > 0) {  // the previous window's slots are merged and its lists read
+      __syncthreads();
+      clear_lists();
+      __syncthreads();
+    }
 
-    // 2. The window's chunk records and unit records.  A unit's record sits
-    // at the window position of its first chunk there (its chunks are
-    // consecutive, so that is t - lc, or 0 for a unit begun before the window).
+    // 2. The window's chunk records, its unit list and its merge tasks.  A
+    // unit's entry is written by the thread of its first chunk in the window:
+    // entry 0 for the window's first unit, 1 for its last (the two that a
+    // window edge may cut), 2.. in any order for the others.  A unit of more
+    // than kBatch chunks here also gets one stage-1 task per batch of kBatch
+    // consecutive slots.
     {
       for (int t = tid; t < n; t += NTH) {
         const int64_t cc = ws + t;
@@ -143,22 +160,34 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         const int h = rem / nb;
         const int lc = rem - h * nb;
         const int valid = min(32, T - 32 * lc);
-        const int lu = t - lc > 0 ? t - lc : 0;
         int* rec = s_rec + t * DS;
         rec[0] = b;
         rec[1] = h;
         rec[2] = lc;
         rec[3] = valid | ((lc == nb - 1 ? 4 : 0) << 8);
-        rec[4] = lu;
         const int last_blk = (T + BS - 1) / BS - 1;
         const int32_t* row = block_tables + static_cast<size_t>(b) * MB;
 #pragma unroll
         for (int j = 0; j < NB; ++j) rec[kRecBase + j] = row[min(lc * kBlocksPerChunk + j, last_blk)];
         if (t == 0 || lc == 0) {  // the unit's first chunk in the window
-          int* ur = s_unit + lu * kUnitWords;
-          ur[0] = t;
-          ur[1] = min(nb - lc, n - t);
-          ur[2] = (lc == 0 && nb <= n - t) ? 1 : 0;
+          const int kk = min(nb - lc, n - t);
+          const int whole = (lc == 0 && nb <= n - t) ? 1 : 0;
+          const int idx = t == 0 ? 0
+                          : t + kk == n
+                              ? 1
+                              : 2 + __hip_atomic_fetch_add(s_misc + 1, 1, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+          int* ue = s_unit + idx * kUnitWords;
+          ue[0] = t | (kk << 12) | (whole << 24);
+          ue[1] = b;
+          ue[2] = h;
+          if (kk > kBatch) {
+            const int nbat = (kk + kBatch - 1) / kBatch;
+            const int base = __hip_atomic_fetch_add(s_misc + 2, nbat, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+            for (int j = 0; j < nbat; ++j)
+              s_task[base + j] = (t + kBatch * j) | (min(kBatch, kk - kBatch * j) << 12);
+          }
         }
       }
       if (tid == 0) s_misc[0] = 0;  // chunk counter
@@ -193,12 +222,12 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       sl8.pos = pos;
     };
 
-    // The merged state of unit (b, hh) over its k window chunks from
-    // position p0, for float4 e of the [G][16][NT] slot layout (head gh).
-    // Slots are read eight at a time (all eight reads in flight) and folded
-    // against a running maximum; the batches and the order within them
-    // depend on kk alone.
-    auto merge_slots = [&](int p0, int kk, int e, int gh, float& mx, float& den, f32x4_t& num) {
+    // The merged state of the kk slots p0, p0 + stride, ... for float4 e of
+    // the [G][16][NT] slot layout (head gh).  Slots are read eight at a time
+    // (all eight reads in flight) and folded against a running maximum; the
+    // batches and the order within them depend on kk alone.
+    auto merge_slots = [&](int p0, int kk, int stride, int e, int gh, float& mx, float& den,
+                           f32x4_t& num) {
       mx = -INFINITY;
       den = 0.f;
       num = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -207,7 +236,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         f32x4_t a[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int p = p0 + min(j0 + t, kk - 1);
+          const int p = p0 + stride * min(j0 + t, kk - 1);
           ml[t] = *reinterpret_cast<const float2*>(s_ml + (p * G + gh) * 2);
           a[t] = *reinterpret_cast<const f32x4_t*>(s_acc + static_cast<size_t>(p) * G * D + 4 * e);
         }
@@ -277,9 +306,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         store_row4(row0 + gh, e, gh, num * (1.0f / den));
       }
     };
-    // Merges unit lu's kk window slots: the output when the unit is whole in
-    // the window, else its piece, published to slot u + x.
-    auto merge_unit = [&](int lu, int kk, int whole, int b, int hh) {
+    // Merges unit (b, hh)'s kk slots lu, lu + stride, ...: the output when the
+    // unit is whole in the window, else its piece, published to slot u + x.
+    auto merge_unit = [&](int lu, int kk, int stride, int whole, int b, int hh) {
       const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hh) * G;
       const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
       float* pacc = prm.part_out + (u + x) * G * D;  // [G][16][NT]
@@ -288,7 +317,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         const int gh = e / E4;
         float mx, den;
         f32x4_t num;
-        merge_slots(lu, kk, e, gh, mx, den, num);
+        merge_slots(lu, kk, stride, e, gh, mx, den, num);
         if (whole) {
           store_row4(row0 + gh, e, gh, num * (1.0f / den));
         } else {
@@ -373,52 +402,69 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
     }
 
-    // 4. Every chunk of the window is in its slot: the wavefronts merge the
-    // window's units, one wavefront per unit.  The units cut by the window's
-    // edges (its first and its last) go to different wavefronts and are
-    // published first; the whole units follow, so the pieces' stores
-    // complete while that work goes on; then the published pieces are
-    // counted and the last piece of each unit merges them all.
+    // 4. Every chunk of the window is in its slot.  Stage 1: every merge
+    // task (kBatch consecutive slots of one unit) is merged in place into the
+    // task's first slot, the tasks spread over all wavefronts.  Stage 2: the
+    // owner of each unit merges its batches (or, for a unit of at most kBatch
+    // chunks here, its slots).  The window's first and last units - the
+    // only ones a window edge can cut - have wavefronts 0 and NW - 1 to
+    // themselves; the others are dealt round robin to the rest.  A cut
+    // unit's piece is published, then counted, and the last piece of each
+    // unit merges them all.  Which wavefront merges what never changes a
+    // result bit: every merge order depends on the unit's chunk count alone.
     __syncthreads();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int nunits = 0;
-    for (int p0 = 0; p0 < n; p0 += 64) {
-      const int p = p0 + lane;
-      nunits += __builtin_popcountll(__ballot(p < n && s_rec[p * DS + 4] == p));
-    }
-    auto owner = [&](int rank) { return rank == nunits - 1 ? NW - 1 : rank % (NW - 1); };
-    int npub = 0, pub_b[2] = {0, 0}, pub_h[2] = {0, 0};
-    for (int pass = 0; pass < 2; ++pass) {  // 0: cut units, 1: whole units
-      int rank = 0;
-      for (int p0 = 0; p0 < n; p0 += 64) {
-        const int p = p0 + lane;
-        uint64_t m = __ballot(p < n && s_rec[p * DS + 4] == p);
-        for (; m != 0; m &= m - 1, ++rank) {
-          const int lu = p0 + __builtin_ctzll(m);
-          if (owner(rank) != w) continue;
-          const int whole = __builtin_amdgcn_readfirstlane(s_unit[lu * kUnitWords + 2]);
-          if (whole != pass) continue;
-          const int kk = __builtin_amdgcn_readfirstlane(s_unit[lu * kUnitWords + 1]);
-          const int b = __builtin_amdgcn_readfirstlane(s_rec[lu * DS]);
-          const int hh = __builtin_amdgcn_readfirstlane(s_rec[lu * DS + 1]);
-          merge_unit(lu, kk, whole, b, hh);
-          if (!whole) {
-            if (npub < 2) {
-              pub_b[npub] = b;
-              pub_h[npub] = hh;
-            }
-            ++npub;
-          }
+    {
+      const int ntask = __builtin_amdgcn_readfirstlane(s_misc[2]);
+      for (int i = w; i < ntask; i += NW) {
+        const int tk = __builtin_amdgcn_readfirstlane(s_task[i]);
+        const int pos = tk & 4095;
+        const int cnt = tk >> 12;
+        for (int e = lane; e < G * E4; e += 64) {
+          const int gh = e / E4;
+          float mx, den;
+          f32x4_t num;
+          merge_slots(pos, cnt, 1, e, gh, mx, den, num);
+          *reinterpret_cast<f32x4_t*>(s_acc + static_cast<size_t>(pos) * G * D + 4 * e) = num;
+          if (e == gh * E4)
+            *reinterpret_cast<float2*>(s_ml + (pos * G + gh) * 2) = make_float2(mx, den);
         }
       }
+      if (ntask > 0) __syncthreads();  // (ntask is the same in every wavefront)
     }
-    // (Only a window's first and last units can be cut, and they have
-    // different owners, so npub <= 1 here; two are handled all the same.)
+    int npub = 0, pub_b = 0, pub_h = 0;
+    auto own_unit = [&](int i) {
+      const int* ue = s_unit + i * kUnitWords;
+      const int e0 = __builtin_amdgcn_readfirstlane(ue[0]);
+      const int kk = (e0 >> 12) & 4095;
+      if (kk == 0) return;  // no last unit apart from the first
+      const int lu = e0 & 4095;
+      const int whole = e0 >> 24;
+      const int b = __builtin_amdgcn_readfirstlane(ue[1]);
+      const int hh = __builtin_amdgcn_readfirstlane(ue[2]);
+      if (kk > kBatch)
+        merge_unit(lu, (kk + kBatch - 1) / kBatch, kBatch, whole, b, hh);
+      else
+        merge_unit(lu, kk, 1, whole, b, hh);
+      if (!whole) {
+        pub_b = b;
+        pub_h = hh;
+        npub = 1;
+      }
+    };
+    if (w == 0) {
+      own_unit(0);
+    } else if (w == NW - 1) {
+      own_unit(1);
+    } else {
+      const int nlist = 2 + __builtin_amdgcn_readfirstlane(s_misc[1]);
+      for (int i = 1 + w; i < nlist; i += NW - 2) own_unit(i);
+    }
     if (npub > 0) {
-      __builtin_amdgcn_s_waitcnt(0);  // the pieces are visible before they are counted
-      for (int t = 0; t < npub && t < 2; ++t) {
-        const int b = t == 0 ? pub_b[0] : pub_b[1];
-        const int hh = t == 0 ? pub_h[0] : pub_h[1];
+      __builtin_amdgcn_s_waitcnt(0);  // the piece is visible before it is counted
+      {
+        const int b = pub_b;
+        const int hh = pub_h;
         const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
         uint32_t prev = 0;
         if (lane == 0)
@@ -492,14 +538,16 @@ WgLayout wg_layout(int head_dim, int block_size, int group, int num_seqs, int ma
   lay.off_misc = w;
   w = up4(w + kMiscWords);
   const int fixed = w;
-  const int per_chunk = kRecBase + nb + kUnitWords + group * head_dim + 2 * group;
-  int cap = (kWgLdsBytes / 4 - fixed - 3 * 4) / per_chunk;
+  const int per_chunk = kRecBase + nb + kUnitWords + 1 + group * head_dim + 2 * group;
+  int cap = (kWgLdsBytes / 4 - fixed - 2 * kUnitWords - 4 * 4) / per_chunk;
   if (cap > kWgMaxCapacity) cap = kWgMaxCapacity;
   lay.capacity = cap;
   lay.off_rec = w;
   w = up4(w + cap * (kRecBase + nb));
   lay.off_unit = w;
-  w = up4(w + cap * kUnitWords);
+  w = up4(w + (cap + 2) * kUnitWords);
+  lay.off_task = w;
+  w = up4(w + cap);
   lay.off_acc = w;
   w = up4(w + cap * group * head_dim);
   lay.off_ml = w;
