@@ -20,9 +20,12 @@
 //     takes fewer; the workgroup's wavefronts finish together.
 //   * Each chunk is folded on its own (a fresh online softmax) and leaves its
 //     (max, sum, accumulator) in an LDS slot of its own.  Once every chunk of
-//     the window is in, the workgroup merges each unit's slots in chunk order
-//     by the rescaled segment rule, one wavefront per unit.  Which wavefront
-//     folded which chunk therefore never changes a result bit.
+//     the window is in, the workgroup merges each unit's slots by the
+//     rescaled segment rule in two stages: batches of eight consecutive slots
+//     (spread over all wavefronts), then each unit's batches in order (by the
+//     unit's owner).  The merge order depends on the unit's chunk count
+//     alone: which wavefront folded or merged what never changes a result
+//     bit.
 //   * A unit that lies wholly in the window is written to the output there.
 //     A unit cut by a window edge is published as a piece (the window's part
 //     of it) and counted; the last piece to arrive merges all of the unit's
