@@ -98,7 +98,8 @@ struct LayerPtrs {
   u32x4_t* v[kMaxCopyLayers];
 };
 
-// grid (pair, layer, K|V); the workgroup streams one block in 16-byte units.
+// grid (pair, layer, K|V); the workgroup streams one block in 16-byte units,
+// four per thread in flight at a time (a 16 KiB block is one round trip).
 __global__ void __launch_bounds__(256)
     copy_blocks_kernel(const LayerPtrs ptrs, const int32_t* __restrict__ block_pairs,
                        int64_t units_per_block) {
@@ -109,7 +110,19 @@ __global__ void __launch_bounds__(256)
   const int64_t dst = block_pairs[2 * pair + 1];
   const u32x4_t* s = base + src * units_per_block;
   u32x4_t* d = base + dst * units_per_block;
-  for (int64_t i = threadIdx.x; i < units_per_block; i += blockDim.x) d[i] = s[i];
+  for (int64_t i0 = threadIdx.x; i0 < units_per_block; i0 += 4 * 256) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t i = i0 + m * 256;
+      if (i < units_per_block) v[m] = s[i];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t i = i0 + m * 256;
+      if (i < units_per_block) d[i] = v[m];
+    }
+  }
 }
 
 // grid (block i, layer, K|V); the workgroup streams one block between the
