@@ -51,6 +51,8 @@ constexpr int kRecBase = 4;    // sequence, KV head, chunk of unit, valid | flag
 constexpr int kUnitWords = 4;  // first window position | chunks << 12 | whole << 24, sequence, head, 0
 constexpr int kMiscWords = 4;  // chunk counter, whole-unit counter, task counter
 constexpr int kBatch = 8;      // slots merged per batch (all their loads in flight at once)
+// Unit entries and tasks pack window positions and chunk counts in 12 bits.
+static_assert(kWgMaxCapacity < 4096, "window positions must fit 12 bits");
 
 template <int D, int BS, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
