@@ -125,6 +125,30 @@ def test_stream_wg_windows(name):
         compare(out.cpu().numpy(), ref, strict_abs=True, what=f"{name} stream_wg w{waves}")
 
 
+# Units of 8, 9, 16, 17, 64 and 65 chunks (the merge batches hold eight
+# slots), single-chunk units and partial last chunks, over two KV heads.
+MERGE_LENS = [8 * 32, 9 * 32 - 3, 16 * 32, 17 * 32 - 31, 64 * 32, 65 * 32 - 1, 1, 2, 31, 33,
+              5 * 32]
+
+
+@pytest.mark.parametrize("waves", [8, 16, 56, 200, 2048])
+def test_stream_wg_merge_batches(waves):
+    """The workgroup kernel's end of window: each unit's chunk slots merged
+    in batches of eight, then the batches, for units whose chunk counts sit
+    on and beside the batch edges; with 1 group (three windows in turn), 2,
+    7, 25 and 256 groups the windows cut those units at many places,
+    including windows inside one unit (cut at both ends).  Repeated calls
+    give the same bits."""
+    say(f"case stream_wg merge batches waves={waves}")
+    w = workloads.random_small(38, len(MERGE_LENS), 8, 2, 64, 16, 0, lens=MERGE_LENS)
+    g, o = GpuSide(w), OracleSide(w)
+    ref = o.decode()
+    out = g.decode(torch.float32, kernel="stream_wg", stream_waves=waves)
+    compare(out.cpu().numpy(), ref, strict_abs=True, what=f"merge batches w{waves}")
+    again = g.decode(torch.float32, kernel="stream_wg", stream_waves=waves)
+    np.testing.assert_array_equal(again.cpu().numpy(), out.cpu().numpy())
+
+
 def test_stream_wg_lengths_over_bound_give_nan():
     """max_seq_len sizes the windows and the workspace; lengths far above it
     (a broken contract) fill the output with NaN instead of overrunning LDS."""

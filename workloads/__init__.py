@@ -268,12 +268,17 @@ def pool_layer_tokens(layer: int, seq: int, length: int, wid: int = 5):
 
 def random_small(seed: int, num_seqs: int, hq: int, hkv: int, d: int, bs: int,
                  max_len: int, min_len: int = 0, slack_blocks: int = 3,
-                 k_mult: float = 1.0) -> Workload:
+                 k_mult: float = 1.0, lens=None) -> Workload:
     """Small random case for parity sweeps: lengths uniform on
-    [min_len, max_len], blocks a random permutation of the pool."""
+    [min_len, max_len] (or the given ``lens``), blocks a random permutation
+    of the pool."""
     wid = 100
-    lens = rng(wid, _ROLE_LENS, seed).integers(min_len, max_len, size=num_seqs,
-                                               endpoint=True).astype(np.int32)
+    if lens is not None:
+        lens = np.asarray(lens, dtype=np.int32)
+        assert len(lens) == num_seqs
+    else:
+        lens = rng(wid, _ROLE_LENS, seed).integers(min_len, max_len, size=num_seqs,
+                                                   endpoint=True).astype(np.int32)
     need = [int(math.ceil(t / bs)) for t in lens]
     pool = sum(need) + slack_blocks
     perm = rng(wid, _ROLE_PERM, seed).permutation(pool).astype(np.int32)
