@@ -367,6 +367,36 @@ pkv_status pkv_paged_prefill(const void* q, const void* k_cache, const void* v_c
                              int32_t block_size, float scale, void* out,
                              const pkv_decode_dims* dims, void* stream);
 
+/* Checkers of the device-resident inputs the calls above take on trust (for
+ * callers that cannot vouch for their tables, e.g. while debugging a block
+ * manager).  Each one clears *flags (device int32, caller-owned), then ORs in
+ * a bit for every kind of violation it finds; the word is final once the
+ * stream reaches the call.  They only compare values: no table entry, slot or
+ * block id is used to address memory, so any values may be checked.  They
+ * enqueue kernels only (no allocation, copy or memset).  Return PKV_OK, or
+ * PKV_ERR_INVALID for a NULL pointer or a negative size, with nothing enqueued.
+ *
+ * Decode inputs [ITH §手動畫一次 block table: a sequence of T tokens uses
+ * logical blocks 0 .. ceil(T/B)-1, each mapped to a physical block]:
+ *   bit 0  an entry of row b in 0 .. ceil(T_b/B)-1 outside [0, num_blocks);
+ *   bit 1  a length outside [0, min(max_seq_len, max_blocks_per_seq*B)]
+ *          (that row's entries are then not examined). */
+pkv_status pkv_check_decode_inputs(const int32_t* block_tables, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, int32_t block_size, int32_t max_seq_len,
+                                   int32_t* flags, void* stream);
+/* Slot mapping of pkv_reshape_and_cache [PU §按 Block 分配: slot =
+ * physical_block * B + offset]: bit 0 a slot >= num_blocks * block_size;
+ * bit 1 a non-negative slot that appears twice (negative slots are padding). */
+pkv_status pkv_check_slot_mapping(const int64_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_blocks, int32_t block_size, int32_t* flags,
+                                  void* stream);
+/* Pairs of pkv_copy_blocks [PU §共享前缀，分叉时 Copy-on-write]: bit 0 a src
+ * or dst outside [0, num_blocks); bit 1 a dst that appears twice; bit 2 a dst
+ * that is also some pair's src. */
+pkv_status pkv_check_block_pairs(const int32_t* block_pairs, int32_t num_pairs,
+                                 int32_t num_blocks, int32_t* flags, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pkv_status_string(int32_t status);
 

@@ -27,6 +27,7 @@ __all__ = [
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
     "BlockManager", "Batcher", "Request", "block_key",
     "PoolExhaustedError", "slot_mapping_for", "PagedKVError", "LIB_PATH",
+    "check_decode_inputs", "check_slot_mapping", "check_block_pairs",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
@@ -107,6 +108,12 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_int
         L.pkv_read_probe.argtypes = [vp, vp, i64, vp, vp]
         L.pkv_read_probe.restype = ctypes.c_int
+        L.pkv_check_decode_inputs.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
+        L.pkv_check_decode_inputs.restype = ctypes.c_int
+        L.pkv_check_slot_mapping.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.pkv_check_slot_mapping.restype = ctypes.c_int
+        L.pkv_check_block_pairs.argtypes = [vp, i32, i32, vp, vp]
+        L.pkv_check_block_pairs.restype = ctypes.c_int
         L.pkv_status_string.argtypes = [i32]
         L.pkv_status_string.restype = ctypes.c_char_p
         L.pkv_abi_version.restype = i32
@@ -556,6 +563,53 @@ def merge_attention_states(part_out: torch.Tensor, part_lse: torch.Tensor,
     if st != PKV_OK:
         raise PagedKVError(st, "pkv_merge_attention_states")
     return out
+
+
+# Checkers of device-resident inputs: each returns the C ABI's violation
+# bit mask (0 when the inputs are consistent), synchronising with the stream.
+
+def _flags_result(st, name, flags, stream) -> int:
+    if st != PKV_OK:
+        raise PagedKVError(st, name)
+    return int(flags.item())
+
+
+def check_decode_inputs(block_tables: torch.Tensor, seq_lens: torch.Tensor, num_blocks: int,
+                        block_size: int, max_seq_len: int, stream=None) -> int:
+    """Bit 0: a used table entry outside [0, num_blocks); bit 1: a length
+    outside [0, min(max_seq_len, max_blocks_per_seq * block_size)]."""
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(seq_lens, "seq_lens", torch.int32, 1)
+    if seq_lens.shape[0] != block_tables.shape[0]:
+        raise ValueError("seq_lens and block_tables disagree on the number of sequences")
+    flags = torch.empty(1, dtype=torch.int32, device=seq_lens.device)
+    st = lib().pkv_check_decode_inputs(block_tables.data_ptr(), seq_lens.data_ptr(),
+                                       seq_lens.shape[0], block_tables.shape[1], num_blocks,
+                                       block_size, max_seq_len, flags.data_ptr(), _stream(stream))
+    return _flags_result(st, "pkv_check_decode_inputs", flags, stream)
+
+
+def check_slot_mapping(slot_mapping: torch.Tensor, num_blocks: int, block_size: int,
+                       stream=None) -> int:
+    """Bit 0: a slot >= num_blocks * block_size; bit 1: a non-negative slot
+    that appears twice."""
+    _check(slot_mapping, "slot_mapping", torch.int64, 1)
+    flags = torch.empty(1, dtype=torch.int32, device=slot_mapping.device)
+    st = lib().pkv_check_slot_mapping(slot_mapping.data_ptr(), slot_mapping.shape[0], num_blocks,
+                                      block_size, flags.data_ptr(), _stream(stream))
+    return _flags_result(st, "pkv_check_slot_mapping", flags, stream)
+
+
+def check_block_pairs(block_pairs: torch.Tensor, num_blocks: int, stream=None) -> int:
+    """Bit 0: a src or dst outside [0, num_blocks); bit 1: a dst that appears
+    twice; bit 2: a dst that is also some pair's src."""
+    _check(block_pairs, "block_pairs", torch.int32, 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [N, 2]")
+    flags = torch.empty(1, dtype=torch.int32, device=block_pairs.device)
+    st = lib().pkv_check_block_pairs(block_pairs.data_ptr(), block_pairs.shape[0], num_blocks,
+                                     flags.data_ptr(), _stream(stream))
+    return _flags_result(st, "pkv_check_block_pairs", flags, stream)
 
 
 def read_probe(src: torch.Tensor, order: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedkv.so")
-SOURCES = ["decode.hip", "decode_wg.hip", "cascade.hip", "prefill.hip", "cache_ops.hip", "probe.hip", "api.cpp"]
+SOURCES = ["decode.hip", "decode_wg.hip", "cascade.hip", "prefill.hip", "cache_ops.hip", "probe.hip", "check.hip", "api.cpp"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are kept out of every kernel (-packed-fp32-ops);

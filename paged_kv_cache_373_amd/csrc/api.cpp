@@ -17,7 +17,7 @@
 namespace {
 
 constexpr int32_t kAbiMajor = 1;
-constexpr int32_t kAbiMinor = 0;
+constexpr int32_t kAbiMinor = 1;
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxGridYZ = 65535;
 
@@ -380,6 +380,41 @@ pkv_status pkv_copy_blocks(void* const* k_caches, void* const* v_caches, int32_t
       return PKV_ERR_INVALID;
   return hip_status(pkv::launch_copy_blocks(k_caches, v_caches, num_layers, block_pairs,
                                             num_pairs, block_bytes,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_check_decode_inputs(const int32_t* block_tables, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, int32_t block_size, int32_t max_seq_len,
+                                   int32_t* flags, void* stream) {
+  if (flags == nullptr || num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+      block_size < 1 || max_seq_len < 0)
+    return PKV_ERR_INVALID;
+  if (num_seqs > 0 && (block_tables == nullptr || seq_lens == nullptr)) return PKV_ERR_INVALID;
+  const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  const int32_t max_len = static_cast<int32_t>(max_seq_len < cap ? max_seq_len : cap);
+  return hip_status(pkv::launch_check_tables(block_tables, seq_lens, num_seqs, max_blocks_per_seq,
+                                             num_blocks, block_size, max_len, flags,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_check_slot_mapping(const int64_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_blocks, int32_t block_size, int32_t* flags,
+                                  void* stream) {
+  if (flags == nullptr || num_tokens < 0 || num_blocks < 1 || block_size < 1)
+    return PKV_ERR_INVALID;
+  if (num_tokens > 0 && slot_mapping == nullptr) return PKV_ERR_INVALID;
+  return hip_status(pkv::launch_check_slots(slot_mapping, num_tokens,
+                                            static_cast<int64_t>(num_blocks) * block_size, flags,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+pkv_status pkv_check_block_pairs(const int32_t* block_pairs, int32_t num_pairs,
+                                 int32_t num_blocks, int32_t* flags, void* stream) {
+  if (flags == nullptr || num_pairs < 0 || num_pairs > 0x7FFFFFFF / 2 || num_blocks < 1)
+    return PKV_ERR_INVALID;
+  if (num_pairs > 0 && block_pairs == nullptr) return PKV_ERR_INVALID;
+  return hip_status(pkv::launch_check_pairs(block_pairs, num_pairs, num_blocks, flags,
                                             static_cast<hipStream_t>(stream)));
 }
 

@@ -174,6 +174,17 @@ struct PrefillLaunch {
   void* out;                   // [num_tokens, Hq, D]
 };
 bool prefill_shape_supported(int head_dim, int block_size, int group);
+
+// Checkers of device-resident inputs (check.hip); each clears *flags, then ORs
+// the violations it finds into it.
+hipError_t launch_check_tables(const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                               int32_t block_size, int32_t max_len, int32_t* flags,
+                               hipStream_t stream);
+hipError_t launch_check_slots(const int64_t* slot_mapping, int32_t num_tokens, int64_t num_slots,
+                              int32_t* flags, hipStream_t stream);
+hipError_t launch_check_pairs(const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
+                              int32_t* flags, hipStream_t stream);
 hipError_t launch_prefill(const PrefillLaunch& a, int max_q_len, hipStream_t stream);
 
 }  // namespace pkv

@@ -232,6 +232,28 @@ def test_read_probe_rejects_before_any_hip_call():
     assert lib.pkv_read_probe(ctypes.c_void_p(0x1008), f, 32, f, None) == pkv.PKV_ERR_INVALID
 
 
+def test_checkers_reject_before_any_hip_call():
+    """The input checkers refuse a NULL flag word, negative sizes and missing
+    arrays with nothing enqueued (no HIP call is made on these paths)."""
+    lib = pkv.lib()
+    f = ctypes.c_void_p(0x1000)
+    inv = pkv.PKV_ERR_INVALID
+    assert lib.pkv_check_decode_inputs(f, f, 2, 4, 10, 16, 64, None, None) == inv
+    assert lib.pkv_check_decode_inputs(f, f, -1, 4, 10, 16, 64, f, None) == inv
+    assert lib.pkv_check_decode_inputs(None, f, 2, 4, 10, 16, 64, f, None) == inv
+    assert lib.pkv_check_decode_inputs(f, f, 2, 0, 10, 16, 64, f, None) == inv
+    assert lib.pkv_check_decode_inputs(f, f, 2, 4, 10, 0, 64, f, None) == inv
+    assert lib.pkv_check_decode_inputs(f, f, 2, 4, 10, 16, -1, f, None) == inv
+    assert lib.pkv_check_slot_mapping(f, 4, 10, 16, None, None) == inv
+    assert lib.pkv_check_slot_mapping(None, 4, 10, 16, f, None) == inv
+    assert lib.pkv_check_slot_mapping(f, -1, 10, 16, f, None) == inv
+    assert lib.pkv_check_slot_mapping(f, 4, 0, 16, f, None) == inv
+    assert lib.pkv_check_block_pairs(f, 3, 10, None, None) == inv
+    assert lib.pkv_check_block_pairs(None, 3, 10, f, None) == inv
+    assert lib.pkv_check_block_pairs(f, -1, 10, f, None) == inv
+    assert lib.pkv_check_block_pairs(f, 3, 0, f, None) == inv
+
+
 def test_writers_reject_before_any_hip_call():
     lib = pkv.lib()
     f = ctypes.c_void_p(0x1000)
