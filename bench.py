@@ -717,6 +717,9 @@ def main() -> int:
             "avg_launch_us": round(decode_ms * 1e3, 3),
         },
     }
+    result["device"] = {"name": torch.cuda.get_device_name(0),
+                        "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+                        "hip": torch.version.hip, "torch": torch.__version__}
     result["trials"] = {"ms_per_step": [round(t, 5) for t in trial_ms],
                         "median": round(ms_step, 5), "min": round(min(trial_ms), 5),
                         "max": round(max(trial_ms), 5)}
