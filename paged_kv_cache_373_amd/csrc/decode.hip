@@ -224,16 +224,17 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
         for (int j = 0; j < k; ++j) mx = fmaxf(mx, sm[gh * k + j]);
         float den = 0.f;
         f32x4_t nm = {0.f, 0.f, 0.f, 0.f};
-        // eight pieces' accumulators in flight at a time
-        for (int j0 = 0; j0 < k; j0 += 8) {
-          f32x4_t a[8];
+        // sixteen pieces' accumulators in flight at a time (the batches
+        // depend on each other only through the sums)
+        for (int j0 = 0; j0 < k; j0 += 16) {
+          f32x4_t a[16];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
+          for (int t = 0; t < 16; ++t) {
             const int j = min(j0 + t, k - 1);
             a[t] = racc.f32x4(static_cast<uint32_t>(((j * G + gh) * D + d0) * sizeof(float)));
           }
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
+          for (int t = 0; t < 16; ++t) {
             if (j0 + t < k) {
               const float f = fast_exp2(sm[gh * k + j0 + t] - mx);
               den += f * sq[gh * k + j0 + t];
