@@ -322,14 +322,11 @@ struct NewToken {
 
 // The new token of a fused decode step sits at position tn = valid - 1 of its
 // unit's last chunk.  Its K and V rows (`nt`, loaded with the chunk) replace
-// that position's operands in `x` - the cache slot has been read but not yet
-// written - and are stored to the slot: block `blk` of the chunk (the one
-// holding position tn), offset tn % BS.  Lane roles as in Mfma.
+// that position's operands in `x`; the cache slot is read, whatever it holds,
+// before or after it is written.  Lane roles as in Mfma.
 template <int D, int BS>
-__device__ __forceinline__ void patch_new_token(const DecodeParams& prm,
-                                                typename Mfma<D, BS>::Regs& x,
-                                                const NewToken<D>& nt, int valid, int hh,
-                                                int blk, int lane) {
+__device__ __forceinline__ void patch_new_operands(typename Mfma<D, BS>::Regs& x,
+                                                   const NewToken<D>& nt, int valid, int lane) {
   using M = Mfma<D, BS>;
   constexpr int HS = M::HS;
   constexpr int NT = M::NT;
@@ -363,19 +360,40 @@ __device__ __forceinline__ void patch_new_token(const DecodeParams& prm,
       for (int e = 0; e < 8; ++e)
         x.v[n][e] = (e == en) ? __builtin_bit_cast(__bf16, nt.v[n]) : x.v[n][e];
   }
+}
+
+// Stores the new token `nt` (position tn of its unit's last chunk) to its
+// cache slot: block `blk` of the chunk (the one holding position tn), KV head
+// hh, offset tn % BS.  Lane roles as in Mfma.
+template <int D, int BS>
+__device__ __forceinline__ void store_new_token(const DecodeParams& prm, const NewToken<D>& nt,
+                                                int tn, int hh, int blk, int lane) {
+  using M = Mfma<D, BS>;
+  const int c = lane >> 4;
+  const int r = lane & 15;
   const size_t tile = (static_cast<size_t>(blk) * prm.num_kv_heads + hh) * M::kTile;
   const int off = tn % BS;
   if (r == 0) {  // lanes (c, 0): dims [32 hs + 8 c, +8) of the K row
 #pragma unroll
-    for (int hs = 0; hs < HS; ++hs)
+    for (int hs = 0; hs < M::HS; ++hs)
       *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 32 * hs + 8 * c) =
           __builtin_bit_cast(u32x4_t, nt.k[hs]);
   }
   if (c == 0) {  // lanes (0, r): features 16 nt + r of the V row
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int n = 0; n < M::NT; ++n)
       prm.v_cache_w[tile + static_cast<size_t>(16 * n + r) * BS + off] = nt.v[n];
   }
+}
+
+// Both steps at once: the operands patched and the slot written.
+template <int D, int BS>
+__device__ __forceinline__ void patch_new_token(const DecodeParams& prm,
+                                                typename Mfma<D, BS>::Regs& x,
+                                                const NewToken<D>& nt, int valid, int hh,
+                                                int blk, int lane) {
+  patch_new_operands<D, BS>(x, nt, valid, lane);
+  store_new_token<D, BS>(prm, nt, valid - 1, hh, blk, lane);
 }
 
 // Sequence lengths into s_len[0, S) and the exclusive prefix of per-sequence

@@ -138,6 +138,13 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     return lo;
   };
 
+  // A fused step's new token, patched into its chunk's operands, whose cache
+  // write is held back: the memory counter retires a wavefront's stores and
+  // loads in issue order, so a store issued among the ring's loads would hold
+  // up every load behind it until the store is acknowledged.
+  NewToken<D> pend;
+  int pend_on = 0, pend_tn = 0, pend_hh = 0, pend_blk = 0;
+
   for (int64_t k = 0; k < wpg; ++k) {
     const int64_t x = static_cast<int64_t>(blockIdx.x) * wpg + k;  // window id
     if (x >= NWeff) break;
@@ -352,8 +359,15 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         NewToken<D> nt;
         nt.load(prm.k_new + row, prm.v_new + row, true, c, r);
         __builtin_amdgcn_s_waitcnt(0);
-        patch_new_token<D, BS>(prm, sl8.x, nt, valid, hh,
-                               __builtin_amdgcn_readfirstlane(rec[kRecBase + tn / BS]), lane);
+        patch_new_operands<D, BS>(sl8.x, nt, valid, lane);
+        // The slot is written when this wavefront has no loads left (a
+        // second new token in the same wavefront writes the first).
+        if (pend_on) store_new_token<D, BS>(prm, pend, pend_tn, pend_hh, pend_blk, lane);
+        pend = nt;
+        pend_on = 1;
+        pend_tn = tn;
+        pend_hh = hh;
+        pend_blk = __builtin_amdgcn_readfirstlane(rec[kRecBase + tn / BS]);
       }
       typename M::State st;
       st.reset();
@@ -487,6 +501,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
     }
   }
+  // Last of all, so that nothing waits for its acknowledgement (written any
+  // earlier, a piece's publication would wait for it).
+  if (pend_on) store_new_token<D, BS>(prm, pend, pend_tn, pend_hh, pend_blk, lane);
 }
 
 // Allows an instantiation the LDS a workgroup may use beyond the default
