@@ -362,39 +362,55 @@ __device__ __forceinline__ void patch_new_operands(typename Mfma<D, BS>::Regs& x
   }
 }
 
-// Stores the new token `nt` (position tn of its unit's last chunk) to its
-// cache slot: block `blk` of the chunk (the one holding position tn), KV head
-// hh, offset tn % BS.  Lane roles as in Mfma.
+// One unit's new token of a fused decode step, written to its cache slot by
+// any one wavefront (the one that reads the unit's last chunk patches its
+// operands instead, so the slot may be read before or after this write).
+// Unit u is sequence u / Hkv, KV head u % Hkv; its token is position T - 1 of
+// a sequence of T >= 1 tokens: block table entry (T - 1) / BS, offset
+// (T - 1) % BS.  load() issues the unit's loads (table entry, K row, V row)
+// as vector loads; store() writes them once they have arrived.
 template <int D, int BS>
-__device__ __forceinline__ void store_new_token(const DecodeParams& prm, const NewToken<D>& nt,
-                                                int tn, int hh, int blk, int lane) {
-  using M = Mfma<D, BS>;
-  const int c = lane >> 4;
-  const int r = lane & 15;
-  const size_t tile = (static_cast<size_t>(blk) * prm.num_kv_heads + hh) * M::kTile;
-  const int off = tn % BS;
-  if (r == 0) {  // lanes (c, 0): dims [32 hs + 8 c, +8) of the K row
+struct TokenWrite {
+  static constexpr int NV = D / 64;  // V features per lane
+  u32x4_t k;                         // lanes l < D / 8: K dims [8 l, 8 l + 8)
+  uint16_t v[NV];                    // lanes l: V features l + 64 j
+  int blk;
+  int on, hh, off;
+  __device__ void load(const DecodeParams& prm, const int32_t* block_tables, int u, int T,
+                       int lane) {
+    constexpr int kRsrcWord3 = 0x00020000;
+    const int Hkv = prm.num_kv_heads;
+    const int b = u / Hkv;
+    hh = u - b * Hkv;
+    on = T >= 1 ? 1 : 0;
+    off = on ? (T - 1) % BS : 0;
+    const int32_t* ent = block_tables + static_cast<size_t>(b) * prm.max_blocks_per_seq +
+                         (on ? (T - 1) / BS : 0);
+    const size_t row = static_cast<size_t>(u) * D;
+    const int bytes = on ? D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(ent), 0, on ? 4 : 0, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(prm.k_new + row), 0, bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(prm.v_new + row), 0, bytes, kRsrcWord3);
+    blk = __builtin_amdgcn_raw_buffer_load_b32(rt, 0, 0, 0);
+    k = __builtin_amdgcn_raw_buffer_load_b128(rk, (lane < D / 8 ? 16 * lane : 0), 0, 0);
 #pragma unroll
-    for (int hs = 0; hs < M::HS; ++hs)
-      *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 32 * hs + 8 * c) =
-          __builtin_bit_cast(u32x4_t, nt.k[hs]);
+    for (int j = 0; j < NV; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b16(rv, 2 * (lane + 64 * j), 0, 0);
   }
-  if (c == 0) {  // lanes (0, r): features 16 nt + r of the V row
+  __device__ void store(const DecodeParams& prm, int lane) const {
+    if (!on) return;
+    const size_t tile =
+        (static_cast<size_t>(__builtin_amdgcn_readfirstlane(blk)) * prm.num_kv_heads + hh) *
+        Mfma<D, BS>::kTile;
+    if (lane < D / 8)
+      *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 8 * lane) = k;
 #pragma unroll
-    for (int n = 0; n < M::NT; ++n)
-      prm.v_cache_w[tile + static_cast<size_t>(16 * n + r) * BS + off] = nt.v[n];
+    for (int j = 0; j < NV; ++j)
+      prm.v_cache_w[tile + static_cast<size_t>(lane + 64 * j) * BS + off] = v[j];
   }
-}
-
-// Both steps at once: the operands patched and the slot written.
-template <int D, int BS>
-__device__ __forceinline__ void patch_new_token(const DecodeParams& prm,
-                                                typename Mfma<D, BS>::Regs& x,
-                                                const NewToken<D>& nt, int valid, int hh,
-                                                int blk, int lane) {
-  patch_new_operands<D, BS>(x, nt, valid, lane);
-  store_new_token<D, BS>(prm, nt, valid - 1, hh, blk, lane);
-}
+};
 
 // Sequence lengths into s_len[0, S) and the exclusive prefix of per-sequence
 // 32-token chunk counts into s_pre[0, S], by all NTH threads of the workgroup

@@ -123,7 +123,27 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
   const int64_t W = static_cast<int64_t>(gridDim.x) * kStreamWaves;
   const int64_t Weff = C < W ? C : W;
   const int64_t g = static_cast<int64_t>(blockIdx.x) * kStreamWaves + w;
-  if (g >= Weff) return;
+  // A fused step's cache writes: wavefront gw of the grid writes the new
+  // tokens of units gw, gw + (all wavefronts), ...  The memory counter retires
+  // a wavefront's stores and loads in issue order, so a store issued among the
+  // ring's loads would hold up every load behind it until it is acknowledged:
+  // the first unit's rows are loaded now and written at the end, after the
+  // pieces' publication, and any further units after that.
+  const int fused = prm.k_new != nullptr ? 1 : 0;
+  const int units = S * Hkv;
+  const int gw = static_cast<int>(g);
+  const int gwaves = static_cast<int>(W);
+  if (g >= Weff) {  // no chunks here: only the writes
+    if (fused)
+      for (int u = gw; u < units; u += gwaves) {
+        TokenWrite<D, BS> more;
+        more.load(prm, block_tables, u, s_len[u / Hkv], lane);
+        more.store(prm, lane);
+      }
+    return;
+  }
+  TokenWrite<D, BS> tw;
+  if (fused && gw < units) tw.load(prm, block_tables, gw, s_len[gw / Hkv], lane);
   const int64_t start = g * C / Weff;
   const int64_t end = (g + 1) * C / Weff;
 
@@ -378,16 +398,9 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       const int valid = __builtin_amdgcn_readlane(cval, i);
       if ((fl & 4) && prm.k_new != nullptr) {
         // The unit's last chunk holds the new token (chunk position
-        // valid - 1): its K/V, loaded with the chunk, replace the operands
-        // (the cache slot was read before it is written), then go to the slot.
-        const int tn = valid - 1;
-        // the chunk's block holding position tn
-        int blk = __builtin_amdgcn_readlane(ent[0], i);
-#pragma unroll
-        for (int j = 1; j < NB; ++j)
-          blk = (tn / BS == j) ? __builtin_amdgcn_readlane(ent[j], i) : blk;
-        patch_new_token<D, BS>(prm, x, sl8.nt, valid, __builtin_amdgcn_readlane(chd, i), blk,
-                               lane);
+        // valid - 1): its K/V, loaded with the chunk, replace the operands,
+        // whether the slot was read before or after its write.
+        patch_new_operands<D, BS>(x, sl8.nt, valid, lane);
       }
       M::step(sl8.q, x, valid, sl, c, st);
       if (fl & 2) finish_piece(__builtin_amdgcn_readlane(clc, i));
@@ -438,6 +451,14 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       unit_span(sb, sh, gf, gl);
       const uint32_t prev = __builtin_amdgcn_readfirstlane(t == 0 ? prev0 : prev1);
       if (prev == static_cast<uint32_t>(gl - gf)) merge_unit(sb, sh);
+    }
+  }
+  if (fused) {
+    if (gw < units) tw.store(prm, lane);
+    for (int u = gw + gwaves; u < units; u += gwaves) {
+      TokenWrite<D, BS> more;
+      more.load(prm, block_tables, u, s_len[u / Hkv], lane);
+      more.store(prm, lane);
     }
   }
 }

@@ -138,12 +138,19 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     return lo;
   };
 
-  // A fused step's new token, patched into its chunk's operands, whose cache
-  // write is held back: the memory counter retires a wavefront's stores and
-  // loads in issue order, so a store issued among the ring's loads would hold
-  // up every load behind it until the store is acknowledged.
-  NewToken<D> pend;
-  int pend_on = 0, pend_tn = 0, pend_hh = 0, pend_blk = 0;
+  // A fused step's cache writes: wavefront gw of the grid writes the new
+  // tokens of units gw, gw + (all wavefronts), ...  The memory counter retires
+  // a wavefront's stores and loads in issue order, so a store issued among the
+  // ring's loads would hold up every load behind it until it is acknowledged
+  // (and a store among the first loads of the whole grid is acknowledged
+  // slowly).  The first unit's rows are loaded now and written at the end;
+  // any further units after that.
+  const int fused = prm.k_new != nullptr ? 1 : 0;
+  const int units = S * Hkv;
+  const int gwave = static_cast<int>(blockIdx.x) * NW + __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gwaves = static_cast<int>(gridDim.x) * NW;
+  TokenWrite<D, BS> tw;
+  if (fused && gwave < units) tw.load(prm, block_tables, gwave, s_len[gwave / Hkv], lane);
 
   for (int64_t k = 0; k < wpg; ++k) {
     const int64_t x = static_cast<int64_t>(blockIdx.x) * wpg + k;  // window id
@@ -349,10 +356,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       const int vf = __builtin_amdgcn_readfirstlane(rec[3]);
       const int valid = vf & 255;
       if (((vf >> 8) & 4) && prm.k_new != nullptr) {
-        // The unit's last chunk holds the new token of a fused decode step.
-        // Its rows are loaded here, which makes this wavefront wait for its
-        // other chunk in flight too; the other wavefronts take up the slack.
-        const int tn = valid - 1;
+        // The unit's last chunk holds the new token of a fused decode step
+        // (position valid - 1), whose rows replace the operands there.  They
+        // are loaded here, which makes this wavefront wait for its other
+        // chunk in flight too; the other wavefronts take up the slack.
         const int hh = __builtin_amdgcn_readfirstlane(rec[1]);
         const size_t row =
             (static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[0])) * Hkv + hh) * D;
@@ -360,14 +367,6 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         nt.load(prm.k_new + row, prm.v_new + row, true, c, r);
         __builtin_amdgcn_s_waitcnt(0);
         patch_new_operands<D, BS>(sl8.x, nt, valid, lane);
-        // The slot is written when this wavefront has no loads left (a
-        // second new token in the same wavefront writes the first).
-        if (pend_on) store_new_token<D, BS>(prm, pend, pend_tn, pend_hh, pend_blk, lane);
-        pend = nt;
-        pend_on = 1;
-        pend_tn = tn;
-        pend_hh = hh;
-        pend_blk = __builtin_amdgcn_readfirstlane(rec[kRecBase + tn / BS]);
       }
       typename M::State st;
       st.reset();
@@ -501,9 +500,13 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
     }
   }
-  // Last of all, so that nothing waits for its acknowledgement (written any
-  // earlier, a piece's publication would wait for it).
-  if (pend_on) store_new_token<D, BS>(prm, pend, pend_tn, pend_hh, pend_blk, lane);
+  if (fused && gwave < units) tw.store(prm, lane);
+  if (fused)
+    for (int u = gwave + gwaves; u < units; u += gwaves) {
+      TokenWrite<D, BS> more;
+      more.load(prm, block_tables, u, s_len[u / Hkv], lane);
+      more.store(prm, lane);
+    }
 }
 
 // Allows an instantiation the LDS a workgroup may use beyond the default
