@@ -404,11 +404,14 @@ struct TokenWrite {
     const size_t tile =
         (static_cast<size_t>(__builtin_amdgcn_readfirstlane(blk)) * prm.num_kv_heads + hh) *
         Mfma<D, BS>::kTile;
+    // Non-temporal: nothing in this launch reads the slot back from the cache.
     if (lane < D / 8)
-      *reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 8 * lane) = k;
+      __builtin_nontemporal_store(
+          k, reinterpret_cast<u32x4_t*>(prm.k_cache_w + tile + off * D + 8 * lane));
 #pragma unroll
     for (int j = 0; j < NV; ++j)
-      prm.v_cache_w[tile + static_cast<size_t>(lane + 64 * j) * BS + off] = v[j];
+      __builtin_nontemporal_store(
+          v[j], &prm.v_cache_w[tile + static_cast<size_t>(lane + 64 * j) * BS + off]);
   }
 };
 
