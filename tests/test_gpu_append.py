@@ -113,6 +113,19 @@ def test_append_token_positions(waves, kernel):
     assert np.all(out[0].cpu().numpy() == 0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("waves", [4, 16])
+@pytest.mark.parametrize("kernel", ["stream", "stream_wg"])
+def test_append_more_units_than_wavefronts(d, waves, kernel):
+    """Each wavefront writes the new tokens of units gw, gw + (all wavefronts),
+    ...: with 40 sequences x 4 KV heads against 4 or 16 wavefronts (the
+    workgroup kernel rounds up to whole workgroups) most wavefronts write
+    several units, some after their chunks, the rest from the end loop."""
+    say(f"case append units>waves d={d} waves={waves} kernel={kernel}")
+    w = workloads.random_small(67, 40, 8, 4, d, 16, 150, min_len=0)
+    _check(w, kernel, f"units>waves d{d} w{waves}", stream_waves=waves)
+
+
 @pytest.mark.parametrize("kernel", ["stream", "stream_wg"])
 def test_two_steps(kernel):
     """Two decode steps back to back: the second appends position T_b (one
