@@ -151,6 +151,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int gwaves = static_cast<int>(gridDim.x) * NW;
   TokenWrite<D, BS> tw;
   if (fused && gwave < units) tw.load(prm, block_tables, gwave, s_len[gwave / Hkv], lane);
+  NewToken<D> nxt;  // the new token of the next chunk to fold, when it holds one
 
   for (int64_t k = 0; k < wpg; ++k) {
     const int64_t x = static_cast<int64_t>(blockIdx.x) * wpg + k;  // window id
@@ -349,6 +350,18 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         }
       }
     };
+    // A fused step's new token of the chunk in `sl8`, if it holds one, into
+    // `nxt` (the chunk is the next one this wavefront folds).
+    auto load_new = [&](const Slot& sl8) {
+      const int* rec = s_rec + sl8.pos * DS;
+      const int vf = __builtin_amdgcn_readfirstlane(rec[3]);
+      if (((vf >> 8) & 4) && prm.k_new != nullptr) {
+        const int hh = __builtin_amdgcn_readfirstlane(rec[1]);
+        const size_t row =
+            (static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[0])) * Hkv + hh) * D;
+        nxt.load(prm.k_new + row, prm.v_new + row, true, c, r);
+      }
+    };
     // Folds the chunk in `sl8` into its LDS slot.
     auto consume = [&](Slot& sl8) {
       const int pos = sl8.pos;
@@ -357,16 +370,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       const int valid = vf & 255;
       if (((vf >> 8) & 4) && prm.k_new != nullptr) {
         // The unit's last chunk holds the new token of a fused decode step
-        // (position valid - 1), whose rows replace the operands there.  They
-        // are loaded here, which makes this wavefront wait for its other
-        // chunk in flight too; the other wavefronts take up the slack.
-        const int hh = __builtin_amdgcn_readfirstlane(rec[1]);
-        const size_t row =
-            (static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[0])) * Hkv + hh) * D;
-        NewToken<D> nt;
-        nt.load(prm.k_new + row, prm.v_new + row, true, c, r);
-        __builtin_amdgcn_s_waitcnt(0);
-        patch_new_operands<D, BS>(sl8.x, nt, valid, lane);
+        // (position valid - 1), whose rows (in `nxt`) replace the operands.
+        patch_new_operands<D, BS>(sl8.x, nxt, valid, lane);
       }
       typename M::State st;
       st.reset();
@@ -397,26 +402,29 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     for (int s = 0; s < DEPTH; ++s) {
       jr[s] = grab();
       issue(jr[s] < n ? jr[s] : 0, ring[s]);
+      if (s == 0) load_new(ring[0]);
     }
     // A wavefront's grabs rise, and it folds its chunks in grab order: once
     // one lies past the window, so do all the ring's later entries.  (The
     // ring is walked with constant indices so its registers stay put.)
-    static_assert(DEPTH >= 1 && DEPTH <= 3, "ring depth");
-    auto advance = [&](Slot& sl8, int& j) {
+    // After each fold the next chunk's new token (if it holds one) is
+    // loaded before the refill, so the fold that needs it waits for nothing
+    // else.
+    static_assert(DEPTH >= 2 && DEPTH <= 3, "ring depth");
+    auto advance = [&](Slot& sl8, int& j, const Slot& next) {
       consume(sl8);
+      load_new(next);
       j = grab();
       issue(j < n ? j : 0, sl8);
     };
     for (;;) {
       if (jr[0] >= n) break;
-      advance(ring[0], jr[0]);
-      if constexpr (DEPTH > 1) {
-        if (jr[1] >= n) break;
-        advance(ring[1], jr[1]);
-      }
+      advance(ring[0], jr[0], ring[1]);
+      if (jr[1] >= n) break;
+      advance(ring[1], jr[1], ring[DEPTH > 2 ? 2 : 0]);
       if constexpr (DEPTH > 2) {
         if (jr[2] >= n) break;
-        advance(ring[2], jr[2]);
+        advance(ring[2], jr[2], ring[0]);
       }
     }
 
