@@ -99,6 +99,13 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
   __shared__ int s_wsum[kStreamWaves];
   constexpr int kMergeStage = 256;  // (max, sum) pairs a wavefront can stage for a merge
   __shared__ float s_mrg[kStreamWaves][2 * kMergeStage];
+  // Output rows of whole units a wavefront holds back until its last load
+  // (a store among the ring's loads holds up every later load until it is
+  // acknowledged, the memory counter retiring them in issue order).
+  constexpr int kStageFloats = 2048;
+  constexpr int kStageUnits = 16;
+  __shared__ float s_out[kStreamWaves][kStageFloats];
+  __shared__ int s_orow[kStreamWaves][kStageUnits];
 
   const int S = prm.num_seqs;
   const int Hkv = prm.num_kv_heads;
@@ -308,12 +315,30 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
   // - one wait for all stores, then both counts - so the chunk ring never
   // drains in mid-range.
   int np_pub = 0, pub_b0 = 0, pub_h0 = 0, pub_b1 = 0, pub_h1 = 0;
+  // whole units' rows held back in s_out[w]: nst of at most scap
+  const int scap = min(kStageUnits, kStageFloats / (G * D));
+  int nst = 0;
   // Ends the current piece whose last chunk is `last_lc` of its unit.
   auto finish_piece = [&](int last_lc) {
     const int T = s_len[pb];
     const int nb = (T + 31) >> 5;
     const size_t row0 = static_cast<size_t>(pb) * Hq + static_cast<size_t>(ph) * G;
-    if (plc0 == 0 && last_lc == nb - 1) {  // the whole unit: final output
+    if (plc0 == 0 && last_lc == nb - 1 && nst < scap) {  // the whole unit, held back
+      float* so = s_out[w] + nst * G * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gh = 4 * c + i;
+        if (gh < G) {
+          const float inv = 1.0f / st.lsum[i];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) so[gh * D + 16 * nt + r] = st.acc[nt][i] * inv;
+        }
+      }
+      if (lane == 0) s_orow[w][nst] = static_cast<int>(row0);
+      ++nst;
+      return;
+    }
+    if (plc0 == 0 && last_lc == nb - 1) {  // the whole unit, no room to hold it back
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int gh = 4 * c + i;
@@ -452,6 +477,12 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       const uint32_t prev = __builtin_amdgcn_readfirstlane(t == 0 ? prev0 : prev1);
       if (prev == static_cast<uint32_t>(gl - gf)) merge_unit(sb, sh);
     }
+  }
+  // the held-back output rows (a unit's G rows are consecutive in the output)
+  for (int k = 0; k < nst; ++k) {
+    const size_t o = static_cast<size_t>(s_orow[w][k]) * D;
+    const float* so = s_out[w] + k * G * D;
+    for (int e = lane; e < G * D; e += 64) store_out(prm.out, o + e, so[e], prm.out_f32);
   }
   if (fused) {
     if (gw < units) tw.store(prm, lane);
