@@ -315,9 +315,16 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
   // - one wait for all stores, then both counts - so the chunk ring never
   // drains in mid-range.
   int np_pub = 0, pub_b0 = 0, pub_h0 = 0, pub_b1 = 0, pub_h1 = 0;
-  // whole units' rows held back in s_out[w]: nst of at most scap
-  const int scap = min(kStageUnits, kStageFloats / (G * D));
+  // The range's first piece (a part of a unit) held back at the end of
+  // s_out[w], laid out as its workspace slot ([G][D] then [G][max, sum]),
+  // when it fits; whole units' rows held back in front of it: nst of at
+  // most scap.
+  const int pfl = G * D + 2 * G;
+  const bool pfit = pfl <= kStageFloats;
+  float* sp = s_out[w] + (pfit ? kStageFloats - pfl : 0);
+  const int scap = min(kStageUnits, (kStageFloats - (pfit ? pfl : 0)) / (G * D));
   int nst = 0;
+  int pheld = 0;
   // Ends the current piece whose last chunk is `last_lc` of its unit.
   auto finish_piece = [&](int last_lc) {
     const int T = s_len[pb];
@@ -351,7 +358,21 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
       }
       return;
     }
-    publish();
+    if (np_pub == 0 && pfit) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gh = 4 * c + i;
+        if (gh < G) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) sp[gh * D + 16 * nt + r] = st.acc[nt][i];
+          if (r == 0) sp[G * D + gh * 2 + 1] = st.lsum[i];
+        }
+      }
+      if (c == 0 && r < G) sp[G * D + r * 2] = st.m2;
+      pheld = 1;
+    } else {
+      publish();
+    }
     if (np_pub == 0) {
       pub_b0 = pb;
       pub_h0 = ph;
@@ -465,6 +486,13 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
 
   // Count the published pieces (their stores complete first) and merge each
   // unit this wavefront closed.
+  if (pheld) {  // publish the held-back first piece
+    const int64_t u = static_cast<int64_t>(pub_b0) * Hkv + pub_h0;
+    float* pacc = prm.part_out + (u + g) * G * D;
+    float* pml = prm.part_ml + (u + g) * G * 2;
+    for (int e = lane; e < G * D; e += 64) store_coherent(pacc + e, sp[e]);
+    if (lane < 2 * G) store_coherent(pml + lane, sp[G * D + lane]);
+  }
   if (np_pub > 0) {
     __builtin_amdgcn_s_waitcnt(0);
     const uint32_t prev0 = count(pub_b0, pub_h0);
