@@ -126,6 +126,20 @@ def test_append_more_units_than_wavefronts(d, waves, kernel):
     _check(w, kernel, f"units>waves d{d} w{waves}", stream_waves=waves)
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(16, 1, 128), (16, 2, 128), (8, 4, 64)])
+@pytest.mark.parametrize("waves", [4, 8])
+def test_stream_held_back_stores(hq, hkv, d, waves):
+    """The per-wavefront kernel holds whole units' output rows and its range's
+    first piece in an LDS area of 2048 floats per wavefront, writing them
+    after its last load: at G = 16, D = 128 the piece does not fit (published
+    at once) and one unit's rows do; at G = 8, D = 128 the piece fits and no
+    rows do; at G = 2, D = 64 many rows fit and the rest are stored at once.
+    Few wavefronts, so each range holds several whole units and cut pieces."""
+    say(f"case stream held-back stores hq={hq} hkv={hkv} d={d} waves={waves}")
+    w = workloads.random_small(68, 24, hq, hkv, d, 16, 260, min_len=0)
+    _check(w, "stream", f"held-back hq{hq} hkv{hkv} d{d} w{waves}", stream_waves=waves)
+
+
 @pytest.mark.parametrize("kernel", ["stream", "stream_wg"])
 def test_two_steps(kernel):
     """Two decode steps back to back: the second appends position T_b (one
