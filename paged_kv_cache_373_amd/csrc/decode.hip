@@ -65,7 +65,9 @@ __device__ __forceinline__ void write_partition_result(const DecodeParams& prm, 
 // [g C / W', (g + 1) C / W') with W' = min(W, C), so every wavefront streams
 // the same number of bytes, to one chunk.  The stretch of a unit inside one
 // wavefront's range is a piece.  A piece that is a whole unit writes the
-// output directly.  Otherwise it publishes (acc, max, sum) into workspace slot
+// output (held in LDS until the wavefront's last load when there is room, as
+// is the range's first piece, the one that ends while chunks are still
+// loading).  Otherwise it publishes (acc, max, sum) into workspace slot
 // u + g (unique: ranges and units both advance with g, so two pieces with the
 // same u + g cannot exist), counts itself on the unit's counter and, if it is
 // the last of the unit's pieces (one per wavefront from the owner of the
