@@ -192,20 +192,9 @@ struct Mfma {
   }
 
   // Issues the loads of one chunk whose NB (block, head) tiles start at the
-  // element offsets `base` (wave-uniform).  kStream: non-temporal loads, for
-  // kernels that read every K/V byte of a call once (decode); kernels that
-  // read a chunk again from the caches (a shared prefix, neighbouring prefill
-  // tiles) keep the default.
-  template <bool kStream = false>
+  // element offsets `base` (wave-uniform).
   static __device__ void load(const uint16_t* k_cache, const uint16_t* v_cache,
                               const size_t (&base)[NB], const Lane& ln, Regs& x) {
-    auto ld = [](const uint16_t* p) {
-      if constexpr (kStream)
-        return __builtin_bit_cast(bf16x8_t,
-                                  __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
-      else
-        return load_bf16x8(p);
-    };
     // base[j] for this lane's block j (a lane constant): two levels of
     // selects on the bits of j, so the choice stays in registers
     auto pick = [&](int j) {
@@ -223,11 +212,11 @@ struct Mfma {
     for (int u = 0; u < 2; ++u) {
       const uint16_t* kp = k_cache + pick(ln.kj[u]) + ln.koff[u];
 #pragma unroll
-      for (int hs = 0; hs < HS; ++hs) x.k[u][hs] = ld(kp + 32 * hs);
+      for (int hs = 0; hs < HS; ++hs) x.k[u][hs] = load_bf16x8(kp + 32 * hs);
     }
     const uint16_t* vp = v_cache + pick(ln.vj) + ln.voff;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) x.v[nt] = ld(vp + 16 * nt * BS);
+    for (int nt = 0; nt < NT; ++nt) x.v[nt] = load_bf16x8(vp + 16 * nt * BS);
   }
 
   // Folds one chunk into the state.  Tokens valid .. 31 of the chunk

@@ -425,7 +425,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         base[j] = static_cast<size_t>(__builtin_amdgcn_readlane(ent[j], i)) * blk_stride + head_off;
-      M::template load<true>(k_cache, v_cache, base, ln, sl8.x);
+      M::load(k_cache, v_cache, base, ln, sl8.x);
       // the chunk's query group travels with it (512 bytes per unit, cached
       // after its first chunk), so a piece starting needs no load of its own
       M::load_q(q, Hq, G, __builtin_amdgcn_readlane(cb, i), hh, c, r, sl8.q);
@@ -613,7 +613,7 @@ __global__ void __launch_bounds__(NW * 64)
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       base[j] = static_cast<size_t>(entry(lbc + j)) * blk_stride + head_off;
-    M::template load<true>(k_cache, v_cache, base, ln, x);
+    M::load(k_cache, v_cache, base, ln, x);
   };
   auto consume = [&](int k, Regs& x) { M::step(qop, x, min(32, span - 32 * k), sl, c, st); };
 

@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       for (int j = 0; j < NB; ++j)
         base[j] = static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[kRecBase + j])) *
                       blk_stride + head_off;
-      M::template load<true>(k_cache, v_cache, base, ln, sl8.x);
+      M::load(k_cache, v_cache, base, ln, sl8.x);
       M::load_q(q, Hq, G, b, hh, c, r, sl8.q);
       sl8.pos = pos;
     };
