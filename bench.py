@@ -127,33 +127,83 @@ def host_cpu() -> str:
 
 
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
-    """The oracle as it stands (fp64 C, OpenMP over (sequence, KV head)) on
-    the host cores, over repetitions of the whole step until ~budget_s."""
+    """The oracle as it stands on the host cores: the paged path (each
+    sequence's K/V gathered through its block table from the paged cache,
+    then dense fp64 attention; OpenMP over (sequence, KV head)) over host
+    copies of the workload's cache and tables, repeated for about budget_s
+    seconds.  Building the host cache is not timed."""
     import oracle
 
+    ko, vo = oracle.new_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    slots = np.array([oracle.slot(w.block_tables[b], t, w.block_size)
+                      for b in range(w.num_seqs) for t in range(int(w.seq_lens[b]))],
+                     dtype=np.int64)
+    oracle.write_cache(ko, vo, w.k_tok, w.v_tok, slots)
     threads = oracle.max_threads()
-    reps, t_total = 0, 0.0
-    while t_total < budget_s and reps < 5000:
-        t0 = time.perf_counter()
-        oracle.dense_decode(w.q, w.k_tok, w.v_tok, w.seq_lens, w.scale, num_threads=threads)
-        t_total += time.perf_counter() - t0
-        reps += 1
-    per = t_total / reps
-    # the same on one thread, over a shorter budget
-    reps1, t1 = 0, 0.0
-    while t1 < budget_s / 3 and reps1 < 5000:
-        t0 = time.perf_counter()
-        oracle.dense_decode(w.q, w.k_tok, w.v_tok, w.seq_lens, w.scale, num_threads=1)
-        t1 += time.perf_counter() - t0
-        reps1 += 1
-    per1 = t1 / reps1
+
+    def run(nthreads, budget):
+        reps, total = 0, 0.0
+        while total < budget and reps < 5000:
+            t0 = time.perf_counter()
+            oracle.paged_decode(w.q, ko, vo, w.block_tables, w.seq_lens, w.scale,
+                                num_threads=nthreads)
+            total += time.perf_counter() - t0
+            reps += 1
+        return reps, total / reps
+
+    reps, per = run(threads, budget_s)
+    reps1, per1 = run(1, budget_s / 3)
     return {"value": round(w.kv_bytes() / per / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"whole {w.name} step ({w.total_tokens} tokens x {w.num_kv_heads} KV heads)"
-                      f" repeated {reps}x, {per * 1e3:.1f} ms each, fp64 gather + dense attention",
+            "sample": f"whole {w.name} step ({w.total_tokens} tokens x {w.num_kv_heads} KV heads):"
+                      f" oracle.paged_decode, K/V gathered through the block tables from the"
+                      f" paged cache then fp64 dense attention, repeated {reps}x,"
+                      f" {per * 1e3:.1f} ms each",
             "single_thread": {"value": round(w.kv_bytes() / per1 / 1e9, 3), "unit": "GB/s",
                               "sample": f"{reps1}x, {per1 * 1e3:.1f} ms each"},
             "host": host_cpu()}
+
+
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_373_amd", "libpkv_probe.so")
+_probe_lib = None
+
+
+def probe_lib():
+    """The benchmark's read-probe library (built beside libpagedkv.so by the
+    package's build step; not part of the attention library's ABI)."""
+    global _probe_lib
+    if _probe_lib is None:
+        import ctypes
+
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is missing: build with python -m "
+                               "paged_kv_cache_373_amd.build")
+        L = ctypes.CDLL(PROBE_LIB)
+        L.pkv_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        L.pkv_probe_read_tiles.restype = ctypes.c_int
+        _probe_lib = L
+    return _probe_lib
+
+
+def read_probe(src, order, sink, stream=None) -> None:
+    """Reads order.numel() 2 KiB tiles of src (uint8 device tensor) in the
+    given order; sink (int32, >= 8 words per tile) gets one folded word per
+    thread.  Every order entry must name a tile inside src (the callers build
+    the orders as permutations of src's tiles; they are not checked here, to
+    keep device reads out of the timed loop)."""
+    import torch
+
+    n = order.numel()
+    if (src.dtype != torch.uint8 or order.dtype != torch.int32 or sink.dtype != torch.int32
+            or n % 32 != 0 or n * 2048 > src.numel() or sink.numel() < 8 * n):
+        raise ValueError("probe: uint8 src holding the tiles, int32 order (a multiple of 32 "
+                         "tiles) and int32 sink of 8 words per tile")
+    st = stream if stream is not None else torch.cuda.current_stream()
+    rc = probe_lib().pkv_probe_read_tiles(src.data_ptr(), order.data_ptr(), n, sink.data_ptr(),
+                                          st.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"pkv_probe_read_tiles returned {rc}")
 
 
 def read_ceiling(pkv, torch, dev, stream, kv_bytes: int, launches: int) -> dict:
@@ -168,20 +218,20 @@ def read_ceiling(pkv, torch, dev, stream, kv_bytes: int, launches: int) -> dict:
               for r in range(regions)]
     sink = torch.empty(tiles * 8, dtype=torch.int32, device=dev)
     for r in range(2 * regions):
-        pkv.read_probe(src, orders[r % regions], sink)
+        read_probe(src, orders[r % regions], sink)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for r in range(launches):
-        pkv.read_probe(src, orders[r % regions], sink)
+        read_probe(src, orders[r % regions], sink)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / launches
     gbs = tiles * 2048 / (ms * 1e-3) / 1e9
     return {"value": round(gbs, 2), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
             "us_per_launch": round(ms * 1e3, 3), "bytes": tiles * 2048,
-            "kind": "trivial read kernel (pkv_read_probe): the step's byte count as 2 KiB "
+            "kind": "trivial read kernel (libpkv_probe.so): the step's byte count as 2 KiB "
                     "tiles in random order, 8 rotated regions, launches back to back"}
 
 
@@ -548,6 +598,9 @@ def main() -> int:
     ap.add_argument("--kernel", default="auto",
                     choices=["auto", "stream_wg", "stream", "mfma", "generic"])
     ap.add_argument("--stream-waves", type=int, default=0)
+    ap.add_argument("--plain-loads", action="store_true",
+                    help="do not pass no_shared_blocks (the workload's tables share no block, "
+                         "so by default the call declares it and K/V stream non-temporally)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB")
     ap.add_argument("--unfused", action="store_true",
                     help="step = reshape_and_cache + paged_attention_decode (two launches)")
@@ -619,8 +672,15 @@ def main() -> int:
     workspace = pkv.DecodeWorkspace(device=dev)
     stream = torch.cuda.current_stream()
 
+    # every physical block of these workloads belongs to one sequence (the
+    # tables are slices of one permutation), which the call may declare
+    no_shared = not args.plain_loads
+    assert len(np.unique(np.concatenate([w.block_tables[b, :-(-int(t) // bs)]
+                                         for b, t in enumerate(w.seq_lens)]))) == \
+        int(sum(-(-int(t) // bs) for t in w.seq_lens)), "a block is shared"
     kw = dict(max_seq_len=max_len, partition_size=ps, waves_per_group=args.waves,
-              kernel=args.kernel, stream_waves=args.stream_waves, workspace=workspace)
+              kernel=args.kernel, stream_waves=args.stream_waves, workspace=workspace,
+              no_shared_blocks=no_shared)
 
     def step(i, ev=None):
         kc, vc = caches[i % copies]
@@ -695,6 +755,7 @@ def main() -> int:
             "head_dim": d, "block_size": bs, "total_tokens": w.total_tokens,
             "kv_bytes_per_step": kv_bytes, "cache_copies_rotated": copies,
             "partition_size": ps or "library", "kernel": kernel_name,
+            "no_shared_blocks": no_shared,
             "step_launches": ("reshape_and_cache + paged_attention_decode" if args.unfused
                               else "paged_attention_decode_append (write + attention fused)"),
             "hbm_peak_frac_of_step": round(value / HBM_PEAK_GBS, 4),

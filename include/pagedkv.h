@@ -126,6 +126,18 @@ typedef struct {
                                  (STREAM: each takes an equal share of the work;
                                  STREAM_WG: rounded up to whole workgroups, each
                                  taking an equal share); 0 = library choice          */
+  int32_t no_shared_blocks;   /* 0 or 1.  1 declares that no physical block is read
+                                 by two sequences of this call (no shared prefix, no
+                                 fork sharing a block): the STREAM and STREAM_WG
+                                 kernels then read K/V with non-temporal loads,
+                                 which do not keep the lines in the caches [PU
+                                 §共享前缀，分叉时 Copy-on-write: forks of one
+                                 prompt point at the same blocks, which caching
+                                 serves for every fork after the first].  Only a
+                                 speed hint: results are identical either way.
+                                 0 (ordinary loads) is always correct.  Ignored by
+                                 the MFMA and GENERIC kernels.  (ABI 2.0; callers
+                                 zero-initialise the whole struct.)                  */
 } pkv_decode_dims;
 
 /* Bytes of scratch that pkv_paged_attention_decode needs for `dims` and
@@ -402,17 +414,6 @@ const char* pkv_status_string(int32_t status);
 
 /* Version of this ABI: (major << 16) | minor. */
 int32_t pkv_abi_version(void);
-
-/* Measurement helper, not part of the attention path: reads num_tiles tiles
- * of 2048 bytes from `src` (device, 16-byte aligned), tile order[i] being the
- * i-th read (order: device int32 [num_tiles], each in range), and writes one
- * folded word per thread to `sink` (device, num_tiles * 8 uint32).  num_tiles
- * must be a positive multiple of 32.  The benchmark times it over the decode
- * step's byte count as the streaming-read ceiling of the cache's access
- * pattern (whole 2 KiB (block, head) tiles in random order).
- * Returns PKV_OK, or an error status with nothing enqueued. */
-pkv_status pkv_read_probe(const void* src, const int32_t* order, int64_t num_tiles,
-                          uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,7 @@ class DecodeDims(ctypes.Structure):
         ("waves_per_group", ctypes.c_int32),
         ("balance_partitions", ctypes.c_int32),
         ("stream_waves", ctypes.c_int32),
+        ("no_shared_blocks", ctypes.c_int32),
     ]
 
 
@@ -106,8 +107,6 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i64,
                                          vp, vp]
             getattr(L, name).restype = ctypes.c_int
-        L.pkv_read_probe.argtypes = [vp, vp, i64, vp, vp]
-        L.pkv_read_probe.restype = ctypes.c_int
         L.pkv_check_decode_inputs.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp]
         L.pkv_check_decode_inputs.restype = ctypes.c_int
         L.pkv_check_slot_mapping.argtypes = [vp, i32, i32, i32, vp, vp]
@@ -154,20 +153,23 @@ def new_kv_cache(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: 
 
 
 def _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
-          waves_per_group, balance_partitions, stream_waves=0) -> DecodeDims:
+          waves_per_group, balance_partitions, stream_waves=0,
+          no_shared_blocks=False) -> DecodeDims:
     s, hq, d = q.shape
     p, hkv, bs, _ = k_cache.shape
     mb = block_tables.shape[1]
     return DecodeDims(s, hq, hkv, d, p, mb, mb * bs if max_seq_len is None else int(max_seq_len),
                       int(partition_size), _DTYPES[out_dtype], _KERNELS[kernel],
-                      int(waves_per_group), int(bool(balance_partitions)), int(stream_waves))
+                      int(waves_per_group), int(bool(balance_partitions)), int(stream_waves),
+                      int(bool(no_shared_blocks)))
 
 
 def decode_workspace_size(q, k_cache, block_tables, *, max_seq_len=None, partition_size=0,
                           out_dtype=torch.bfloat16, kernel="auto", waves_per_group=0,
-                          balance_partitions=False, stream_waves=0) -> int:
+                          balance_partitions=False, stream_waves=0,
+                          no_shared_blocks=False) -> int:
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
-                 waves_per_group, balance_partitions, stream_waves)
+                 waves_per_group, balance_partitions, stream_waves, no_shared_blocks)
     n = lib().pkv_decode_workspace_size(ctypes.byref(dims), k_cache.shape[2])
     if n == ctypes.c_size_t(-1).value:
         raise PagedKVError(PKV_ERR_INVALID, "pkv_decode_workspace_size")
@@ -176,11 +178,12 @@ def decode_workspace_size(q, k_cache, block_tables, *, max_seq_len=None, partiti
 
 def decode_plan_kernel(q, k_cache, block_tables, *, max_seq_len=None, partition_size=0,
                        out_dtype=torch.bfloat16, kernel="auto", waves_per_group=0,
-                       balance_partitions=False, stream_waves=0) -> str:
+                       balance_partitions=False, stream_waves=0,
+                       no_shared_blocks=False) -> str:
     """Name of the kernel family a decode call with these arguments runs
     (what ``kernel="auto"`` resolves to)."""
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out_dtype, kernel,
-                 waves_per_group, balance_partitions, stream_waves)
+                 waves_per_group, balance_partitions, stream_waves, no_shared_blocks)
     k = lib().pkv_decode_plan_kernel(ctypes.byref(dims), k_cache.shape[2])
     names = {v: n for n, v in _KERNELS.items()}
     if k not in names or k == 0:
@@ -188,15 +191,21 @@ def decode_plan_kernel(q, k_cache, block_tables, *, max_seq_len=None, partition_
     return names[k]
 
 
+def _torch_stream(stream):
+    """The torch stream object for a call's ``stream`` argument (torch's
+    current stream when None)."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(_stream(stream))
+
+
 def _zero_prefix(buf: torch.Tensor, n: int, stream) -> None:
     """Clear buf[:n] with a fill kernel on ``stream`` (torch's current stream
-    when None)."""
-    if stream is None:
-        buf[:n].zero_()
-        return
-    st = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(
-        _stream(stream))
-    with torch.cuda.stream(st):
+    when None), so the clearing is ordered before the call that follows on
+    that stream."""
+    with torch.cuda.stream(_torch_stream(stream)):
         buf[:n].zero_()
 
 
@@ -207,6 +216,13 @@ class DecodeWorkspace:
     previous call's partial results.  The object remembers how many leading
     bytes are known to be zero and clears more (with a fill kernel on the
     call's stream) only when a call needs a larger counter region.
+
+    One workspace serves calls on one stream at a time (the C ABI's rule:
+    calls that may overlap need different workspaces).  A grown buffer is
+    allocated and zeroed on the stream of the call that needs it, and every
+    stream that uses the buffer is recorded with the allocator, so a buffer
+    that is replaced is not reused while work queued on such a stream may
+    still touch it.
 
     ``buffer`` may wrap an existing uint8 device tensor of any contents; by
     default the workspace allocates and grows its own zero-filled buffer."""
@@ -219,15 +235,24 @@ class DecodeWorkspace:
         self.device = buffer.device if buffer is not None else device
         self.zeroed = 0  # leading bytes known to be zero
         self.growable = buffer is None
+        self._streams = set()  # streams (by handle) recorded on the current buffer
 
     def prepare(self, nbytes: int, zeroed_bytes: int, device, stream=None) -> torch.Tensor:
+        st = _torch_stream(stream)
         if self.buffer is None or self.buffer.numel() < nbytes:
             if not self.growable:
                 raise ValueError(f"workspace holds {self.buffer.numel()} bytes, call needs {nbytes}")
-            self.buffer = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            with torch.cuda.stream(st):
+                self.buffer = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             self.zeroed = self.buffer.numel()
-        if zeroed_bytes > self.zeroed:
-            _zero_prefix(self.buffer, zeroed_bytes, stream)
+            self._streams = {st.cuda_stream}
+        elif zeroed_bytes > self.zeroed:
+            _zero_prefix(self.buffer, zeroed_bytes, st)
+        if st.cuda_stream not in self._streams and not torch.cuda.is_current_stream_capturing():
+            # (under graph capture the graph's replays are ordered by the
+            # caller; the buffer stays referenced by this object meanwhile)
+            self.buffer.record_stream(st)
+            self._streams.add(st.cuda_stream)
         # after the call: the counter region is zero again, the partial
         # results behind it are not
         if nbytes > 0:
@@ -238,8 +263,10 @@ class DecodeWorkspace:
 _ws_cache = {}
 
 
-def _default_workspace(device: torch.device) -> DecodeWorkspace:
-    key = (device.type, device.index)
+def _default_workspace(device: torch.device, stream) -> DecodeWorkspace:
+    """The workspace a call without one uses: one per (device, stream), so
+    calls on different streams never share counters."""
+    key = (device.type, device.index, _torch_stream(stream).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None:
         ws = DecodeWorkspace(device=device)
@@ -247,9 +274,28 @@ def _default_workspace(device: torch.device) -> DecodeWorkspace:
     return ws
 
 
+_plan_cache = {}
+
+
+def _decode_sizes(dims: DecodeDims, bs: int):
+    """(workspace bytes, zeroed bytes) of a decode call, cached per dims."""
+    key = (bytes(dims), bs)
+    hit = _plan_cache.get(key)
+    if hit is None:
+        L = lib()
+        need = L.pkv_decode_workspace_size(ctypes.byref(dims), bs)
+        if need == ctypes.c_size_t(-1).value:
+            raise PagedKVError(PKV_ERR_INVALID, "pkv_paged_attention_decode")
+        hit = (int(need), int(L.pkv_decode_workspace_zeroed_bytes(ctypes.byref(dims), bs)))
+        if len(_plan_cache) > 4096:
+            _plan_cache.clear()
+        _plan_cache[key] = hit
+    return hit
+
+
 def _decode(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale, out,
             max_seq_len, partition_size, kernel, waves_per_group, balance_partitions,
-            stream_waves, workspace, stream) -> torch.Tensor:
+            stream_waves, no_shared_blocks, workspace, stream) -> torch.Tensor:
     _check(q, "q", torch.bfloat16, 3)
     _check(k_cache, "k_cache", torch.bfloat16, 4)
     _check(v_cache, "v_cache", torch.bfloat16, 4)
@@ -270,16 +316,13 @@ def _decode(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_siz
         if tuple(k_new.shape) != (s, hkv, d) or tuple(v_new.shape) != (s, hkv, d):
             raise ValueError("k_new and v_new must be [S, Hkv, D]")
     dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out.dtype, kernel,
-                 waves_per_group, balance_partitions, stream_waves)
+                 waves_per_group, balance_partitions, stream_waves, no_shared_blocks)
     L = lib()
-    need = L.pkv_decode_workspace_size(ctypes.byref(dims), bs)
-    if need == ctypes.c_size_t(-1).value:
-        raise PagedKVError(PKV_ERR_INVALID, "pkv_paged_attention_decode")
-    zeroed = L.pkv_decode_workspace_zeroed_bytes(ctypes.byref(dims), bs)
+    need, zeroed = _decode_sizes(dims, bs)
     ws_ptr, ws_len = None, 0
     if need:
         if workspace is None:
-            workspace = _default_workspace(q.device)
+            workspace = _default_workspace(q.device, stream)
         if isinstance(workspace, DecodeWorkspace):
             buf = workspace.prepare(need, zeroed, q.device, stream)
         else:
@@ -313,17 +356,19 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            scale: float, out: torch.Tensor, *, max_seq_len: Optional[int] = None,
                            partition_size: int = 0, kernel: str = "auto",
                            waves_per_group: int = 0, balance_partitions: bool = False,
-                           stream_waves: int = 0, workspace=None,
-                           stream=None) -> torch.Tensor:
+                           stream_waves: int = 0, no_shared_blocks: bool = False,
+                           workspace=None, stream=None) -> torch.Tensor:
     """Single-query paged decode attention ([ITH §PagedAttention 的核心想法];
     [PU §按 Block 分配]).  Writes ``out`` [S, Hq, D] (bf16 or fp32) and returns
     it.  ``max_seq_len`` defaults to the table capacity (max_blocks * B).
+    ``no_shared_blocks=True`` declares that no physical block is read by two
+    of the call's sequences (a speed hint; see ``pkv_decode_dims``).
     ``workspace`` is a :class:`DecodeWorkspace` (reused across calls; the
-    default is one per device) or a raw uint8 device tensor, whose counter
-    region is then cleared before every call."""
+    default is one per device and stream) or a raw uint8 device tensor, whose
+    counter region is then cleared before every call."""
     return _decode(q, None, None, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
                    out, max_seq_len, partition_size, kernel, waves_per_group,
-                   balance_partitions, stream_waves, workspace, stream)
+                   balance_partitions, stream_waves, no_shared_blocks, workspace, stream)
 
 
 def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -333,6 +378,7 @@ def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
                                   max_seq_len: Optional[int] = None, partition_size: int = 0,
                                   kernel: str = "auto", waves_per_group: int = 0,
                                   balance_partitions: bool = False, stream_waves: int = 0,
+                                  no_shared_blocks: bool = False,
                                   workspace=None, stream=None) -> torch.Tensor:
     """One decode step: writes k_new/v_new [S, Hkv, D] (the token at position
     T_b - 1 of each sequence) into the slot its block table gives, then
@@ -340,7 +386,7 @@ def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: t
     分配]).  With the stream kernel both happen in one launch."""
     return _decode(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
                    out, max_seq_len, partition_size, kernel, waves_per_group,
-                   balance_partitions, stream_waves, workspace, stream)
+                   balance_partitions, stream_waves, no_shared_blocks, workspace, stream)
 
 
 def cascade_workspace_size(q, k_cache, block_tables, num_groups: int, max_prefix_len: int, *,
@@ -610,20 +656,3 @@ def check_block_pairs(block_pairs: torch.Tensor, num_blocks: int, stream=None) -
     st = lib().pkv_check_block_pairs(block_pairs.data_ptr(), block_pairs.shape[0], num_blocks,
                                      flags.data_ptr(), _stream(stream))
     return _flags_result(st, "pkv_check_block_pairs", flags, stream)
-
-
-def read_probe(src: torch.Tensor, order: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
-    """Measurement helper: read ``order.numel()`` 2 KiB tiles of ``src`` (a
-    uint8 device tensor) in the given order; ``sink`` (int32, numel >= 8 x
-    tiles) receives one folded word per thread.  Not part of the attention
-    path: the benchmark's streaming-read ceiling."""
-    _check(src, "src", torch.uint8, 1)
-    _check(order, "order", torch.int32, 1)
-    _check(sink, "sink", torch.int32, 1)
-    n = order.numel()
-    if n % 32 != 0 or sink.numel() < 8 * n:
-        raise ValueError("order must hold a multiple of 32 tiles and sink 8 words per tile")
-    st = lib().pkv_read_probe(src.data_ptr(), order.data_ptr(), n, sink.data_ptr(),
-                              _stream(stream))
-    if st != PKV_OK:
-        raise PagedKVError(st, "pkv_read_probe")

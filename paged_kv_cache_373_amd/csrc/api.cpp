@@ -16,8 +16,8 @@
 
 namespace {
 
-constexpr int32_t kAbiMajor = 1;
-constexpr int32_t kAbiMinor = 1;
+constexpr int32_t kAbiMajor = 2;
+constexpr int32_t kAbiMinor = 0;
 constexpr size_t kAlign = 256;
 constexpr int32_t kMaxGridYZ = 65535;
 
@@ -84,6 +84,7 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
     return p;
   if (d->balance_partitions != 0 && d->balance_partitions != 1) return p;
   if (d->stream_waves < 0 || d->stream_waves % 4 != 0) return p;
+  if (d->no_shared_blocks != 0 && d->no_shared_blocks != 1) return p;
   if (d->num_seqs > kMaxGridYZ || d->num_kv_heads > kMaxGridYZ || d->num_q_heads > kMaxGridYZ)
     return (p.status = PKV_ERR_UNSUPPORTED, p);
   p.group = d->num_q_heads / d->num_kv_heads;
@@ -238,10 +239,10 @@ int32_t pkv_decode_plan_kernel(const pkv_decode_dims* dims, int32_t block_size) 
 
 }  // extern "C"
 
-namespace {
+namespace pkv {
 
 // Shared by the decode entry points; k_new / v_new are null for a plain decode.
-pkv_status decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+pkv_status decode_entry(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                        const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
                        int32_t block_size, float scale, void* out, const pkv_decode_dims* dims,
                        void* workspace, size_t workspace_bytes, void* stream) {
@@ -282,6 +283,7 @@ pkv_status decode_impl(const void* q, const void* k_new, const void* v_new, cons
   a.prm.num_partitions = p.num_partitions;
   a.prm.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
   a.prm.out_f32 = dims->out_dtype == PKV_DTYPE_F32 ? 1 : 0;
+  a.prm.stream_kv = dims->no_shared_blocks;
   a.prm.out = out;
   if (p.workspace_bytes > 0) {
     char* ws = static_cast<char*>(workspace);
@@ -316,7 +318,7 @@ pkv_status decode_impl(const void* q, const void* k_new, const void* v_new, cons
   }
 }
 
-}  // namespace
+}  // namespace pkv
 
 extern "C" {
 
@@ -325,7 +327,7 @@ pkv_status pkv_paged_attention_decode(const void* q, const void* k_cache, const 
                                       int32_t block_size, float scale, void* out,
                                       const pkv_decode_dims* dims, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, block_tables, seq_lens, block_size,
+  return pkv::decode_entry(q, nullptr, nullptr, k_cache, v_cache, block_tables, seq_lens, block_size,
                      scale, out, dims, workspace, workspace_bytes, stream);
 }
 
@@ -341,7 +343,7 @@ pkv_status pkv_paged_attention_decode_append(const void* q, const void* k_new, c
     if (!p.ok) return p.status;
     return dims->num_seqs == 0 ? PKV_OK : PKV_ERR_INVALID;
   }
-  return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
+  return pkv::decode_entry(q, k_new, v_new, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
                      out, dims, workspace, workspace_bytes, stream);
 }
 
@@ -416,15 +418,6 @@ pkv_status pkv_check_block_pairs(const int32_t* block_pairs, int32_t num_pairs,
   if (num_pairs > 0 && block_pairs == nullptr) return PKV_ERR_INVALID;
   return hip_status(pkv::launch_check_pairs(block_pairs, num_pairs, num_blocks, flags,
                                             static_cast<hipStream_t>(stream)));
-}
-
-pkv_status pkv_read_probe(const void* src, const int32_t* order, int64_t num_tiles,
-                          uint32_t* sink, void* stream) {
-  if (num_tiles <= 0 || num_tiles % 32 != 0 || num_tiles / 32 > 0x7FFFFFFF) return PKV_ERR_INVALID;
-  if (src == nullptr || order == nullptr || sink == nullptr || !aligned16(src))
-    return PKV_ERR_INVALID;
-  return hip_status(
-      pkv::launch_read_probe(src, order, num_tiles, sink, static_cast<hipStream_t>(stream)));
 }
 
 pkv_status pkv_merge_attention_states(const float* part_out, const float* part_lse,

@@ -38,6 +38,20 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
 
+// A K/V tile load: an ordinary load, or (kStream) a non-temporal one, which
+// tells the caches the line will not be read again soon.  Streaming loads pay
+// off only when no other sequence of the call reads the same physical block
+// (no shared prefix): a block several sequences share is served from the
+// caches for all but its first reader only with ordinary loads.
+template <bool kStream>
+__device__ __forceinline__ bf16x8_t load_kv(const uint16_t* p) {
+  const u32x4_t* a = reinterpret_cast<const u32x4_t*>(p);
+  if constexpr (kStream)
+    return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(a));
+  else
+    return __builtin_bit_cast(bf16x8_t, *a);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
@@ -192,7 +206,8 @@ struct Mfma {
   }
 
   // Issues the loads of one chunk whose NB (block, head) tiles start at the
-  // element offsets `base` (wave-uniform).
+  // element offsets `base` (wave-uniform); kStream selects non-temporal loads.
+  template <bool kStream = false>
   static __device__ void load(const uint16_t* k_cache, const uint16_t* v_cache,
                               const size_t (&base)[NB], const Lane& ln, Regs& x) {
     // base[j] for this lane's block j (a lane constant): two levels of
@@ -212,11 +227,11 @@ struct Mfma {
     for (int u = 0; u < 2; ++u) {
       const uint16_t* kp = k_cache + pick(ln.kj[u]) + ln.koff[u];
 #pragma unroll
-      for (int hs = 0; hs < HS; ++hs) x.k[u][hs] = load_bf16x8(kp + 32 * hs);
+      for (int hs = 0; hs < HS; ++hs) x.k[u][hs] = load_kv<kStream>(kp + 32 * hs);
     }
     const uint16_t* vp = v_cache + pick(ln.vj) + ln.voff;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) x.v[nt] = load_bf16x8(vp + 16 * nt * BS);
+    for (int nt = 0; nt < NT; ++nt) x.v[nt] = load_kv<kStream>(vp + 16 * nt * BS);
   }
 
   // Folds one chunk into the state.  Tokens valid .. 31 of the chunk

@@ -83,7 +83,7 @@ __device__ __forceinline__ void write_partition_result(const DecodeParams& prm, 
 constexpr int kStreamWaves = 4;       // wavefronts per workgroup, each with its own range
 constexpr int kStreamMaxSeqs = 2048;  // sequences whose lengths and prefix fit in LDS
 
-template <int D, int BS>
+template <int D, int BS, bool kStream>
 __global__ void __launch_bounds__(kStreamWaves * 64)
     __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1))) decode_stream(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
                   const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -425,7 +425,7 @@ __global__ void __launch_bounds__(kStreamWaves * 64)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         base[j] = static_cast<size_t>(__builtin_amdgcn_readlane(ent[j], i)) * blk_stride + head_off;
-      M::load(k_cache, v_cache, base, ln, sl8.x);
+      M::template load<kStream>(k_cache, v_cache, base, ln, sl8.x);
       // the chunk's query group travels with it (512 bytes per unit, cached
       // after its first chunk), so a piece starting needs no load of its own
       M::load_q(q, Hq, G, __builtin_amdgcn_readlane(cb, i), hh, c, r, sl8.q);
@@ -910,22 +910,23 @@ hipError_t launch_mfma_bs(const DecodeLaunch& a, int waves, dim3 grid, hipStream
   }
 }
 
+template <int D, int BS>
+void launch_stream_k(const DecodeLaunch& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kStreamWaves * 64);
+  if (a.prm.stream_kv != 0)
+    decode_stream<D, BS, true><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache,
+                                                           a.block_tables, a.seq_lens, a.prm);
+  else
+    decode_stream<D, BS, false><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache,
+                                                            a.block_tables, a.seq_lens, a.prm);
+}
+
 template <int D>
 hipError_t launch_stream_bs(const DecodeLaunch& a, dim3 grid, hipStream_t stream) {
-  const dim3 block(kStreamWaves * 64);
   switch (a.prm.block_size) {
-    case 8:
-      decode_stream<D, 8><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache, a.block_tables,
-                                                      a.seq_lens, a.prm);
-      break;
-    case 16:
-      decode_stream<D, 16><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache, a.block_tables,
-                                                       a.seq_lens, a.prm);
-      break;
-    default:
-      decode_stream<D, 32><<<grid, block, 0, stream>>>(a.q, a.k_cache, a.v_cache, a.block_tables,
-                                                       a.seq_lens, a.prm);
-      break;
+    case 8: launch_stream_k<D, 8>(a, grid, stream); break;
+    case 16: launch_stream_k<D, 16>(a, grid, stream); break;
+    default: launch_stream_k<D, 32>(a, grid, stream); break;
   }
   return hipGetLastError();
 }

@@ -54,7 +54,7 @@ constexpr int kBatch = 8;      // slots merged per batch (all their loads in fli
 // Unit entries and tasks pack window positions and chunk counts in 12 bits.
 static_assert(kWgMaxCapacity < 4096, "window positions must fit 12 bits");
 
-template <int D, int BS, int NW>
+template <int D, int BS, int NW, bool kStream>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
     decode_wg(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
               const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       for (int j = 0; j < NB; ++j)
         base[j] = static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[kRecBase + j])) *
                       blk_stride + head_off;
-      M::load(k_cache, v_cache, base, ln, sl8.x);
+      M::template load<kStream>(k_cache, v_cache, base, ln, sl8.x);
       M::load_q(q, Hq, G, b, hh, c, r, sl8.q);
       sl8.pos = pos;
     };
@@ -519,37 +519,39 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
 
 // Allows an instantiation the LDS a workgroup may use beyond the default
 // dynamic allowance (once per process; repeated calls set the same value).
-template <int D, int BS, int NW>
+template <int D, int BS, int NW, bool kStream>
 hipError_t allow_lds() {
   static const hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&decode_wg<D, BS, NW>),
+      reinterpret_cast<const void*>(&decode_wg<D, BS, NW, kStream>),
       hipFuncAttributeMaxDynamicSharedMemorySize, kWgLdsBytes);
   return e;
+}
+
+template <int D, int BS, int NW, bool kStream>
+hipError_t launch_wg(const DecodeLaunch& a, int groups, const WgLayout& lay, size_t lds,
+                     hipStream_t stream) {
+  const hipError_t e = allow_lds<D, BS, NW, kStream>();
+  if (e != hipSuccess) return e;
+  decode_wg<D, BS, NW, kStream><<<dim3(groups), dim3(NW * 64), lds, stream>>>(
+      a.q, a.k_cache, a.v_cache, a.block_tables, a.seq_lens, a.prm, lay);
+  return hipGetLastError();
 }
 
 template <int D, int NW>
 hipError_t launch_wg_bs(const DecodeLaunch& a, int groups, const WgLayout& lay, size_t lds,
                         hipStream_t stream) {
-  const dim3 grid(groups), block(NW * 64);
-  const hipError_t e = a.prm.block_size == 8    ? allow_lds<D, 8, NW>()
-                       : a.prm.block_size == 16 ? allow_lds<D, 16, NW>()
-                                                : allow_lds<D, 32, NW>();
-  if (e != hipSuccess) return e;
+  const bool st = a.prm.stream_kv != 0;
   switch (a.prm.block_size) {
     case 8:
-      decode_wg<D, 8, NW><<<grid, block, lds, stream>>>(a.q, a.k_cache, a.v_cache,
-                                                         a.block_tables, a.seq_lens, a.prm, lay);
-      break;
+      return st ? launch_wg<D, 8, NW, true>(a, groups, lay, lds, stream)
+                : launch_wg<D, 8, NW, false>(a, groups, lay, lds, stream);
     case 16:
-      decode_wg<D, 16, NW><<<grid, block, lds, stream>>>(a.q, a.k_cache, a.v_cache,
-                                                          a.block_tables, a.seq_lens, a.prm, lay);
-      break;
+      return st ? launch_wg<D, 16, NW, true>(a, groups, lay, lds, stream)
+                : launch_wg<D, 16, NW, false>(a, groups, lay, lds, stream);
     default:
-      decode_wg<D, 32, NW><<<grid, block, lds, stream>>>(a.q, a.k_cache, a.v_cache,
-                                                          a.block_tables, a.seq_lens, a.prm, lay);
-      break;
+      return st ? launch_wg<D, 32, NW, true>(a, groups, lay, lds, stream)
+                : launch_wg<D, 32, NW, false>(a, groups, lay, lds, stream);
   }
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pagedkv.h"
+
 namespace pkv {
 
 // Everything a decode kernel needs besides the tensor pointers.
@@ -22,6 +24,8 @@ struct DecodeParams {
   int32_t num_partitions;     // grid extent over partitions = ceil(max_seq_len / partition_size)
   float scale_log2;           // scale * log2(e): scores live in base-2 units inside the kernels
   int32_t out_f32;            // 1: out is fp32, 0: out is bf16
+  int32_t stream_kv;          // 1: no physical block is read by two sequences of the
+                              // call, so the stream kernels read K/V non-temporally
   void* out;                  // [S, Hq, D]
   // Split-KV workspace.  Partitioned kernels (only when num_partitions > 1):
   // partition results per (sequence, q head, partition).  Stream kernels: one
@@ -50,6 +54,15 @@ struct DecodeLaunch {
   int32_t num_seqs;
   DecodeParams prm;
 };
+
+// The decode entry points' common body (in api.cpp): host checks, the plan,
+// then the launch.  k_new / v_new are null for a plain decode.  `workspace`
+// must satisfy the workspace contract of pkv_paged_attention_decode.
+pkv_status decode_entry(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                        const void* v_cache, const int32_t* block_tables,
+                        const int32_t* seq_lens, int32_t block_size, float scale, void* out,
+                        const pkv_decode_dims* dims, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 // Shapes the kernels are instantiated for.
 bool mfma_shape_supported(int head_dim, int block_size, int group, int partition_size);
@@ -99,11 +112,6 @@ hipError_t launch_reshape_and_cache(const uint16_t* k, const uint16_t* v,
                                     const int64_t* slot_mapping, int32_t num_tokens,
                                     int32_t num_kv_heads, int32_t head_dim, uint16_t* k_cache,
                                     uint16_t* v_cache, int32_t block_size, hipStream_t stream);
-
-// Measurement helper: reads num_tiles 2 KiB tiles of src in the order given
-// (num_tiles a multiple of 32; sink holds num_tiles * 8 words).
-hipError_t launch_read_probe(const void* src, const int32_t* order, int64_t num_tiles,
-                             uint32_t* sink, hipStream_t stream);
 
 constexpr int kMaxCopyLayers = 64;
 // Swap: blocks block_ids[0..n) of every layer's K and V cache to (to_host = 1)

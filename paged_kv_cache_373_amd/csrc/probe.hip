@@ -1,14 +1,13 @@
-// probe.hip - a trivial read kernel that measures the streaming-read ceiling
-// the decode kernels are held against: it reads whole 2 KiB tiles (one
-// (block, head) K or V tile at B = 16, D = 64) in a caller-given order and
-// does nothing with them but fold them into one word per thread.  Not part of
-// the attention path; the benchmark reports its rate as context.
+// probe.hip - the benchmark's read probe, built on its own into
+// libpkv_probe.so (not part of libpagedkv.so or its C ABI).
+//
+// A trivial read kernel that measures the streaming-read ceiling the decode
+// kernels are held against: it reads whole 2 KiB tiles (one (block, head) K
+// or V tile at B = 16, D = 64) in a caller-given order and does nothing with
+// them but fold them into one word per thread.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "internal.h"
-
-namespace pkv {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -42,11 +41,21 @@ __global__ void __launch_bounds__(kProbeThreads)
 
 }  // namespace
 
-hipError_t launch_read_probe(const void* src, const int32_t* order, int64_t num_tiles,
-                             uint32_t* sink, hipStream_t stream) {
+// Reads num_tiles tiles of 2048 bytes from `src` (device, 16-byte aligned),
+// tile order[i] (device int32, each in range) being the i-th read, and writes
+// one folded word per thread to `sink` (device, num_tiles * 8 uint32).
+// num_tiles must be a positive multiple of 32.  Returns 0, -1 for an invalid
+// argument (nothing enqueued) or -4 for a launch error.
+extern "C" int pkv_probe_read_tiles(const void* src, const int32_t* order, int64_t num_tiles,
+                                    uint32_t* sink, void* stream) {
+  if (num_tiles <= 0 || num_tiles % kProbeTilesPerGroup != 0 ||
+      num_tiles / kProbeTilesPerGroup > 0x7FFFFFFF)
+    return -1;
+  if (src == nullptr || order == nullptr || sink == nullptr ||
+      (reinterpret_cast<uintptr_t>(src) & 15u) != 0)
+    return -1;
   const dim3 grid(static_cast<unsigned>(num_tiles / kProbeTilesPerGroup));
-  read_tiles<<<grid, kProbeThreads, 0, stream>>>(static_cast<const u32x4_t*>(src), order, sink);
-  return hipGetLastError();
+  read_tiles<<<grid, kProbeThreads, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const u32x4_t*>(src), order, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }
-
-}  // namespace pkv

@@ -54,12 +54,12 @@ def test_header_compiles_as_c():
 
 
 def test_struct_layout_matches_binding():
-    assert ctypes.sizeof(pkv.DecodeDims) == 13 * 4
+    assert ctypes.sizeof(pkv.DecodeDims) == 14 * 4
 
 
 def test_version_and_status_strings():
     lib = pkv.lib()
-    assert lib.pkv_abi_version() >> 16 == 1
+    assert lib.pkv_abi_version() >> 16 == 2
     for code in (0, -1, -2, -3, -4, 7):
         assert lib.pkv_status_string(code)
 
@@ -219,17 +219,6 @@ def test_append_rejects_before_any_hip_call():
     assert call(f, None) == pkv.PKV_ERR_INVALID
     assert call(ctypes.c_void_p(0x1008), f) == pkv.PKV_ERR_INVALID  # misaligned k_new
     assert call(f, f, _dims(num_q_heads=30)) == pkv.PKV_ERR_INVALID
-
-
-def test_read_probe_rejects_before_any_hip_call():
-    lib = pkv.lib()
-    f = ctypes.c_void_p(0x1000)
-    lib.pkv_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                   ctypes.c_void_p, ctypes.c_void_p]
-    assert lib.pkv_read_probe(f, f, 0, f, None) == pkv.PKV_ERR_INVALID
-    assert lib.pkv_read_probe(f, f, 48, f, None) == pkv.PKV_ERR_INVALID  # not a multiple of 32
-    assert lib.pkv_read_probe(None, f, 32, f, None) == pkv.PKV_ERR_INVALID
-    assert lib.pkv_read_probe(ctypes.c_void_p(0x1008), f, 32, f, None) == pkv.PKV_ERR_INVALID
 
 
 def test_checkers_reject_before_any_hip_call():

@@ -344,24 +344,57 @@ def test_workspace_reuse_across_shapes():
         assert int(raw[:z].count_nonzero()) == 0
 
 
-def test_read_probe_folds_every_tile():
-    """The measurement helper reads each tile it is given: thread t of
-    workgroup g folds 16 bytes of each of its 16 tiles (XOR of 4 words)."""
-    say("case read probe")
-    r = np.random.default_rng(9)
-    tiles = 64
-    src = r.integers(0, 2**32, size=(tiles * 2048) // 4, dtype=np.uint32)
-    order = r.permutation(tiles).astype(np.int32)
-    sink = torch.zeros(tiles * 8, dtype=torch.int32, device=DEV)
-    pkv.read_probe(torch.from_numpy(src.view(np.uint8)).to(DEV), torch.from_numpy(order).to(DEV),
-                   sink)
-    words = src.reshape(tiles, 128, 4)  # tile, 16-byte piece, word
-    exp = np.zeros((tiles // 32, 256), dtype=np.uint32)
-    for g in range(tiles // 32):
-        for t in range(256):
-            half, l = divmod(t, 128)
-            x = 0
-            for j in range(16):
-                x ^= int(np.bitwise_xor.reduce(words[order[32 * g + 2 * j + half], l]))
-            exp[g, t] = x
-    np.testing.assert_array_equal(sink.cpu().numpy().view(np.uint32).reshape(-1, 256), exp)
+@pytest.mark.parametrize("kernel", ["auto", "stream_wg", "stream"])
+def test_no_shared_blocks_hint_is_bit_identical(kernel):
+    """The streaming-load hint changes only how K/V are loaded: outputs are
+    the same bits with and without it (plain decode and fused step), and
+    within tolerance of the oracle."""
+    say(f"case no_shared_blocks hint kernel={kernel}")
+    w = workloads.random_small(91, 24, 32, 8, 64, 16, 2500, min_len=1)
+    g, o = GpuSide(w), OracleSide(w)
+    a = g.decode(torch.float32, kernel=kernel)
+    b = g.decode(torch.float32, kernel=kernel, no_shared_blocks=True)
+    assert torch.equal(a, b)
+    compare(b.cpu().numpy(), o.decode(), strict_abs=True, what=f"hint/{kernel}")
+    cu = w.cu_seqlens
+    k_new = bits_to_bf16(w.k_tok[cu[1:] - 1]).to(DEV)
+    v_new = bits_to_bf16(w.v_tok[cu[1:] - 1]).to(DEV)
+    outs = []
+    for hint in (False, True):
+        out = torch.empty_like(a)
+        pkv.paged_attention_decode_append(g.q, k_new, v_new, g.kc, g.vc, g.bt, g.lens,
+                                          w.block_size, w.scale, out,
+                                          max_seq_len=int(w.seq_lens.max()), kernel=kernel,
+                                          no_shared_blocks=hint)
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], a)  # the new tokens are the cached ones: same result
+
+
+def test_workspace_grown_on_a_side_stream():
+    """A decode on a stream other than torch's current one, with a
+    DecodeWorkspace that grows for it: the buffer is allocated and zeroed on
+    that stream, so the counters are zero when the kernel starts.  Repeated
+    with a larger call (the workspace grows again) and against the default
+    per-stream workspace."""
+    say("case workspace grown on a side stream")
+    side = torch.cuda.Stream()
+    ws = pkv.DecodeWorkspace(device=DEV)
+    for seed, s_, mx in ((92, 6, 300), (93, 40, 3000)):
+        w = workloads.random_small(seed, s_, 32, 8, 64, 16, mx, min_len=1)
+        g, o = GpuSide(w), OracleSide(w)
+        ref = o.decode()
+        torch.cuda.synchronize()
+        outs = []
+        for wsp in (ws, None):
+            out = torch.empty((w.num_seqs, w.num_q_heads, w.head_dim), dtype=torch.float32,
+                              device=DEV)
+            side.wait_stream(torch.cuda.current_stream())
+            pkv.paged_attention_decode(g.q, g.kc, g.vc, g.bt, g.lens, w.block_size, w.scale, out,
+                                       max_seq_len=int(w.seq_lens.max()), workspace=wsp,
+                                       stream=side)
+            side.synchronize()
+            outs.append(out)
+        for out in outs:
+            compare(out.cpu().numpy(), ref, strict_abs=True, what=f"side stream S={s_}")
+        assert torch.equal(outs[0], outs[1])

@@ -155,7 +155,9 @@ def test_pool_scale_16_layers(block_size):
     the last one and attends - with paged_attention_decode_append on even
     layers and reshape_and_cache(slot_mapping) + paged_attention_decode on odd
     ones.  Sampled sequences of every layer are checked against the oracle:
-    their cache rows bit-exact through the table, their outputs in tolerance."""
+    their cache rows bit-exact through the table, their outputs in tolerance.
+    In layers 0 (fused step) and 1 (writer, then decode) every sequence's
+    output is compared; every layer's output must be finite."""
     w = workloads.pool_step(block_size)
     S, hq, hkv, d, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     say(f"case workload pool16 B={bs}: {int(w.seq_lens.sum())} tokens per layer, "
@@ -195,9 +197,16 @@ def test_pool_scale_16_layers(block_size):
             pkv.paged_attention_decode(q, kc, vc, btd, lens, bs, w.scale, out,
                                        max_seq_len=int(w.seq_lens.max()))
         torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all()), f"B={bs} layer {layer}: non-finite output"
         got = out.float().cpu().numpy()
         ktok = bf16_bits(kt)
         vtok = bf16_bits(vt)
+        if layer < 2:
+            # every sequence of the layer against the oracle
+            ref_all = oracle.dense_decode(qb, ktok, vtok, w.seq_lens, w.scale)
+            compare(got, ref_all, strict_abs=False,
+                    what=f"B={bs} layer {layer} all {S} sequences "
+                         f"({'fused step' if layer % 2 == 0 else 'writer + decode'})")
         for b in sample:
             T = int(w.seq_lens[b])
             rows = np.arange(cu[b], cu[b + 1])
