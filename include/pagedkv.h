@@ -230,6 +230,34 @@ pkv_status pkv_paged_attention_decode_append(const void* q, const void* k_new, c
                                              void* workspace, size_t workspace_bytes,
                                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * call as pkv_paged_attention_decode, same arguments and results, except that
+ * its split-KV scratch is a fixed array inside the library instead of a
+ * caller workspace.  It allocates nothing (no hipMalloc, no allocating
+ * library routine) and enqueues only kernels on `stream`.
+ *   Limit: a call whose workspace (pkv_decode_workspace_size for the same
+ *   dims and block_size) exceeds PKV_NOALLOC_SCRATCH_BYTES is rejected with
+ *   PKV_ERR_WORKSPACE, nothing enqueued.
+ *   The array: one per device (the device of `stream`; the current device for
+ *   the null stream), PKV_NOALLOC_SCRATCH_BYTES bytes, held until the process
+ *   ends.  Every call on a device shares it and leaves its partial results in
+ *   it; the library clears what must start at zero (with a small kernel on
+ *   `stream`, ordered before the call's own kernels).  Calls that may overlap
+ *   on one device (different streams, or host threads, without ordering
+ *   between them) race on it: order them, or use pkv_paged_attention_decode
+ *   with one workspace each.
+ * Returns PKV_OK, PKV_ERR_INVALID / PKV_ERR_UNSUPPORTED as the workspace
+ * variant, PKV_ERR_WORKSPACE when the scratch would not fit, PKV_ERR_HIP when
+ * the device or the array's address cannot be obtained or a launch fails. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+pkv_status pkv_paged_attention_decode_noalloc(const void* q, const void* k_cache,
+                                              const void* v_cache,
+                                              const int32_t* block_tables,
+                                              const int32_t* seq_lens, int32_t block_size,
+                                              float scale, void* out,
+                                              const pkv_decode_dims* dims, void* stream);
+
 /* Slot-mapped cache write [ITH §手動畫一次 block table: the next token goes
  * into the tail block's next free slot; PU §按 Block 分配: new tokens fill the
  * tail block first].  For n in [0, num_tokens) with s = slot_mapping[n] >= 0:

@@ -21,7 +21,8 @@ from .block_manager import BlockManager, PoolExhaustedError, block_key, slot_map
 from .scheduler import Batcher, Request
 
 __all__ = [
-    "lib", "paged_attention_decode", "paged_attention_decode_append", "reshape_and_cache",
+    "lib", "paged_attention_decode", "paged_attention_decode_append",
+    "paged_attention_decode_noalloc", "reshape_and_cache",
     "copy_blocks", "cascade_decode", "cascade_workspace_size", "paged_prefill", "swap_out",
     "swap_in", "swap_buffer",
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.pkv_paged_attention_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32,
                                                         ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.pkv_paged_attention_decode_append.restype = ctypes.c_int
+        L.pkv_paged_attention_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, ctypes.c_float,
+                                                         vp, dims_p, vp]
+        L.pkv_paged_attention_decode_noalloc.restype = ctypes.c_int
         L.pkv_reshape_and_cache.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, i32, i32, vp]
         L.pkv_reshape_and_cache.restype = ctypes.c_int
         L.pkv_copy_blocks.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, vp, i32, i64,
@@ -369,6 +373,46 @@ def paged_attention_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     return _decode(q, None, None, k_cache, v_cache, block_tables, seq_lens, block_size, scale,
                    out, max_seq_len, partition_size, kernel, waves_per_group,
                    balance_partitions, stream_waves, no_shared_blocks, workspace, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, block_tables: torch.Tensor,
+                                   seq_lens: torch.Tensor, block_size: int, scale: float,
+                                   out: torch.Tensor, *, max_seq_len: Optional[int] = None,
+                                   partition_size: int = 0, kernel: str = "auto",
+                                   waves_per_group: int = 0, balance_partitions: bool = False,
+                                   stream_waves: int = 0, no_shared_blocks: bool = False,
+                                   stream=None) -> torch.Tensor:
+    """:func:`paged_attention_decode` for callers that cannot allocate: the
+    split-KV scratch is the library's fixed per-device array (at most
+    ``NOALLOC_SCRATCH_BYTES``), so nothing is allocated here or in the
+    library.  Calls that may overlap on one device race on that array."""
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(v_cache, "v_cache", torch.bfloat16, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(seq_lens, "seq_lens", torch.int32, 1)
+    if out.dtype not in _DTYPES:
+        raise TypeError("out must be bf16 or fp32")
+    _check(out, "out", out.dtype, 3)
+    s, hq, d = q.shape
+    p, hkv, bs, d2 = k_cache.shape
+    if bs != block_size or d2 != d or tuple(v_cache.shape) != (p, hkv, d, bs):
+        raise ValueError("cache shapes must be k [P,Hkv,B,D] and v [P,Hkv,D,B] matching q")
+    if tuple(out.shape) != (s, hq, d) or block_tables.shape[0] != s or seq_lens.shape[0] != s:
+        raise ValueError("q, out, block_tables and seq_lens disagree on the batch")
+    dims = _dims(q, k_cache, block_tables, max_seq_len, partition_size, out.dtype, kernel,
+                 waves_per_group, balance_partitions, stream_waves, no_shared_blocks)
+    st = lib().pkv_paged_attention_decode_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        seq_lens.data_ptr(), bs, float(scale), out.data_ptr(), ctypes.byref(dims),
+        _stream(stream))
+    if st != PKV_OK:
+        raise PagedKVError(st, "pkv_paged_attention_decode_noalloc")
+    return out
 
 
 def paged_attention_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

@@ -22,7 +22,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpagedkv.so")
 PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
 SOURCES = ["decode.hip", "decode_wg.hip", "cascade.hip", "prefill.hip", "cache_ops.hip",
-           "check.hip", "api.cpp"]
+           "check.hip", "noalloc.hip", "api.cpp"]
 PROBE_SOURCES = ["probe.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
