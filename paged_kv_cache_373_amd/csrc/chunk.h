@@ -192,17 +192,22 @@ struct Mfma {
     }
   };
 
-  // Query group of KV head `kvh` of sequence b as the QK^T B operand.
+  // Query group of KV head `kvh` of sequence b as the QK^T B operand.  The
+  // loads go through a buffer resource that spans the group's G rows: lanes
+  // of rows r >= G address past its end and read zeros, so no instruction
+  // touches the operand between its load and the matrix-core op that uses it
+  // (a select there would make the wavefront wait for the load early).
   static __device__ void load_q(const uint16_t* q, int Hq, int G, int b, int kvh, int c, int r,
                                 bf16x8_t (&qop)[HS]) {
-    const uint16_t* qrow =
-        q + (static_cast<size_t>(b) * Hq + kvh * G + (r < G ? r : 0)) * D + 8 * c;
+    constexpr int kRsrcWord3 = 0x00020000;
+    const uint16_t* grp = q + (static_cast<size_t>(b) * Hq + static_cast<size_t>(kvh) * G) * D;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(grp), 0, G * D * 2, kRsrcWord3);
+    const int off = (r * D + 8 * c) * 2;
 #pragma unroll
-    for (int hs = 0; hs < HS; ++hs) qop[hs] = load_bf16x8(qrow + 32 * hs);
-    if (r >= G) {
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) qop[hs] = bf16x8_t{};
-    }
+    for (int hs = 0; hs < HS; ++hs)
+      qop[hs] = __builtin_bit_cast(bf16x8_t,
+                                   __builtin_amdgcn_raw_buffer_load_b128(rq, off + 64 * hs, 0, 0));
   }
 
   // Issues the loads of one chunk whose NB (block, head) tiles start at the

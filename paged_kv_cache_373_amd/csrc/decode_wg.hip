@@ -19,17 +19,23 @@
 //     in LDS, so a wavefront that the hardware serves more slowly simply
 //     takes fewer; the workgroup's wavefronts finish together.
 //   * Each chunk is folded on its own (a fresh online softmax) and leaves its
-//     (max, sum, accumulator) in an LDS slot of its own.  Once every chunk of
-//     the window is in, the workgroup merges each unit's slots by the
-//     rescaled segment rule in two stages: batches of eight consecutive slots
-//     (spread over all wavefronts), then each unit's batches in order (by the
-//     unit's owner).  The merge order depends on the unit's chunk count
-//     alone: which wavefront folded or merged what never changes a result
-//     bit.
-//   * A unit that lies wholly in the window is written to the output there.
-//     A unit cut by a window edge is published as a piece (the window's part
-//     of it) and counted; the last piece to arrive merges all of the unit's
-//     pieces in window order, as in the stream kernel.
+//     (max, sum, accumulator) in an LDS slot of its own, then counts itself
+//     in its batch: eight consecutive slots of its unit.  The wavefront that
+//     counts a batch's last chunk merges the batch into the batch's first
+//     slot right away, while its other chunk is loading.  The streaming loop
+//     touches nothing but LDS besides its loads: a global store or atomic
+//     inside it would leave loads and stores pending together on the
+//     wavefront's memory counter, and the compiler then waits for every load
+//     in flight before each fold.
+//   * Once every chunk of the window is in, each unit's batches (at most
+//     eight slots) are merged by one wavefront, all in slot order: the order
+//     depends on the unit's chunk count alone, so which wavefront folded or
+//     merged what never changes a result bit.  The window's first and last
+//     units, the only ones a window edge can cut, have wavefronts of their
+//     own.  A unit that lies wholly in the window is written to the output.
+//     A cut unit is published as a piece (the window's part of it) and
+//     counted on a device counter; the last piece to arrive merges all of
+//     the unit's pieces in window order.
 //
 // A window holds at most `capacity` chunks (the LDS slots).  When the call's
 // chunks need more, each workgroup walks several windows in turn, with a
@@ -45,14 +51,25 @@ namespace pkv {
 namespace {
 
 // Words (4 bytes) of LDS per window chunk besides its state: the chunk
-// record (kRecBase + NB words), a unit-list entry (kUnitWords) and a merge
-// task (1 word).
-constexpr int kRecBase = 4;    // sequence, KV head, chunk of unit, valid | flags << 8
-constexpr int kUnitWords = 4;  // first window position | chunks << 12 | whole << 24, sequence, head, 0
-constexpr int kMiscWords = 4;  // chunk counter, whole-unit counter, task counter
-constexpr int kBatch = 8;      // slots merged per batch (all their loads in flight at once)
-// Unit entries and tasks pack window positions and chunk counts in 12 bits.
+// record (kRecBase + NB words) and a unit-list entry (kUnitWords).
+constexpr int kRecBase = 5;    // sequence, KV head, unit's first window position | its chunks
+                               // here << 12, valid | last << 8 | entry << 12, batch count
+constexpr int kUnitWords = 4;  // first window position | chunks << 12 | whole << 24, sequence,
+                               // head, unused
+constexpr int kBatch = 8;      // slots merged together (all their reads in flight at once)
+constexpr int kMiscWords = 4;  // chunk counter, first and last units' chunks, middle units
+// Unit entries pack window positions and chunk counts in 12 bits.
 static_assert(kWgMaxCapacity < 4096, "window positions must fit 12 bits");
+
+// LDS-only ordering: the slot writes of a fold are complete before its count
+// is, and a merge reads slots only after the count that completed them.
+// Vector-memory loads in flight are not waited for.
+__device__ __forceinline__ void lds_release() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+}
+__device__ __forceinline__ void lds_acquire() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <int D, int BS, int NW, bool kStream>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
@@ -69,6 +86,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   constexpr int kBlocksPerChunk = 32 / BS;
   constexpr int DS = kRecBase + NB;  // words per chunk record
   constexpr int E4 = D / 4;          // float4s per head in a state slot
+  constexpr int kMaxIt = (16 * E4 + 63) / 64;  // float4s of a slot per lane at the largest group
 
   extern __shared__ __align__(16) int lds[];
   int* s_len = lds + lay.off_len;
@@ -76,8 +94,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   int* s_wsum = lds + lay.off_wsum;
   int* s_misc = lds + lay.off_misc;
   int* s_rec = lds + lay.off_rec;
-  int* s_unit = lds + lay.off_unit;  // unit list: [0] first unit, [1] last unit, [2..] the rest
-  int* s_task = lds + lay.off_task;  // stage-1 merge tasks: first slot | slots << 12
+  int* s_unit = lds + lay.off_unit;  // unit entries: [0] first unit, [1] last unit, [2 + t] the rest
+  int* s_list = lds + lay.off_list;  // entries of the units between the first and the last
   float* s_acc = reinterpret_cast<float*>(lds + lay.off_acc);  // [capacity][G][16][NT]
   float* s_ml = reinterpret_cast<float*>(lds + lay.off_ml);    // [capacity][G][max, sum]
 
@@ -91,14 +109,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   const int c = lane >> 4;
   const int r = lane & 15;
 
-  // The window's list counters and its last-unit entry start empty (the
-  // prefix's barriers order this before the first window's records).
-  auto clear_lists = [&]() {
-    if (tid < 2) s_misc[1 + tid] = 0;
-    if (tid < kUnitWords) s_unit[kUnitWords + tid] = 0;
-  };
-  clear_lists();
-  // 1. Lengths and the chunk prefix; the windows of this workgroup.
+  // 1. Lengths and the chunk prefix; the windows of this workgroup.  (The
+  // middle-unit counter starts at zero; the prefix's barriers order this
+  // before the first window's records.)
+  if (tid == 0) s_misc[3] = 0;
   chunk_prefix<NTH>(seq_lens, S, s_len, s_pre, s_wsum, tid);
   const int64_t C = static_cast<int64_t>(Hkv) * s_pre[S];
   const int64_t NWG = gridDim.x;
@@ -137,6 +151,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     }
     return lo;
   };
+  // Unit of global chunk cc and the chunk's index in it.
+  auto locate = [&](int64_t cc, int& b, int& h, int& lc) {
+    b = seq_of(cc);
+    const int nb = (s_len[b] + 31) >> 5;
+    const int rem = static_cast<int>(cc - static_cast<int64_t>(Hkv) * s_pre[b]);
+    h = rem / nb;
+    lc = rem - h * nb;
+  };
 
   // A fused step's cache writes: wavefront gw of the grid writes the new
   // tokens of units gw, gw + (all wavefronts), ...  The memory counter retires
@@ -158,56 +180,50 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     if (x >= NWeff) break;
     const int64_t ws = x * C / NWeff;
     const int n = static_cast<int>((x + 1) * C / NWeff - ws);
-    if (k > 0) {  // the previous window's slots are merged and its lists read
+    if (k > 0) {  // the previous window's slots, records and lists are done with
       __syncthreads();
-      clear_lists();
+      if (tid == 0) s_misc[3] = 0;
       __syncthreads();
     }
 
-    // 2. The window's chunk records, its unit list and its merge tasks.  A
-    // unit's entry is written by the thread of its first chunk in the window:
-    // entry 0 for the window's first unit, 1 for its last (the two that a
-    // window edge may cut), 2.. in any order for the others.  A unit of more
-    // than kBatch chunks here also gets one stage-1 task per batch of kBatch
-    // consecutive slots.
+    // 2. The window's chunk records and its unit list.  Unit entry 0 is the
+    // window's first unit, 1 its last (unused when the window holds one
+    // unit), 2 + t the unit between them whose first chunk sits at window
+    // position t: a unit's chunks are consecutive in the window, so each
+    // chunk finds its unit's entry, and the unit's chunk count in the window,
+    // from its own position and index alone.  The entries of the units
+    // between go to a list as well, in any order.
     {
       for (int t = tid; t < n; t += NTH) {
-        const int64_t cc = ws + t;
-        const int b = seq_of(cc);
+        int b, h, lc;
+        locate(ws + t, b, h, lc);
         const int T = s_len[b];
         const int nb = (T + 31) >> 5;
-        const int rem = static_cast<int>(cc - static_cast<int64_t>(Hkv) * s_pre[b]);
-        const int h = rem / nb;
-        const int lc = rem - h * nb;
         const int valid = min(32, T - 32 * lc);
+        const int first = max(t - lc, 0);       // the unit's first chunk in the window
+        const int end = min(t - lc + nb, n);     // and one past its last
+        const int kk = end - first;
+        const int ui = first == 0 ? 0 : (end == n ? 1 : 2 + first);
         int* rec = s_rec + t * DS;
         rec[0] = b;
         rec[1] = h;
-        rec[2] = lc;
-        rec[3] = valid | ((lc == nb - 1 ? 4 : 0) << 8);
+        rec[2] = first | (kk << 12);
+        rec[3] = valid | ((lc == nb - 1 ? 4 : 0) << 8) | (ui << 12);
+        rec[4] = 0;
         const int last_blk = (T + BS - 1) / BS - 1;
         const int32_t* row = block_tables + static_cast<size_t>(b) * MB;
 #pragma unroll
         for (int j = 0; j < NB; ++j) rec[kRecBase + j] = row[min(lc * kBlocksPerChunk + j, last_blk)];
-        if (t == 0 || lc == 0) {  // the unit's first chunk in the window
-          const int kk = min(nb - lc, n - t);
-          const int whole = (lc == 0 && nb <= n - t) ? 1 : 0;
-          const int idx = t == 0 ? 0
-                          : t + kk == n
-                              ? 1
-                              : 2 + __hip_atomic_fetch_add(s_misc + 1, 1, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_WORKGROUP);
-          int* ue = s_unit + idx * kUnitWords;
-          ue[0] = t | (kk << 12) | (whole << 24);
+        if (t == first) {  // the unit's first chunk in the window writes its entry
+          const int whole = (lc == 0 && end - first == nb) ? 1 : 0;
+          int* ue = s_unit + ui * kUnitWords;
+          ue[0] = first | (kk << 12) | (whole << 24);
           ue[1] = b;
           ue[2] = h;
-          if (kk > kBatch) {
-            const int nbat = (kk + kBatch - 1) / kBatch;
-            const int base = __hip_atomic_fetch_add(s_misc + 2, nbat, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_WORKGROUP);
-            for (int j = 0; j < nbat; ++j)
-              s_task[base + j] = (t + kBatch * j) | (min(kBatch, kk - kBatch * j) << 12);
-          }
+          ue[3] = 0;
+          if (ui >= 2)
+            s_list[__hip_atomic_fetch_add(s_misc + 3, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_WORKGROUP)] = ui;
         }
       }
       if (tid == 0) s_misc[0] = 0;  // chunk counter
@@ -243,8 +259,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     };
 
     // The merged state of the kk slots p0, p0 + stride, ... for float4 e of
-    // the [G][16][NT] slot layout (head gh).  Slots are read eight at a time
-    // (all eight reads in flight) and folded against a running maximum; the
+    // the [G][16][NT] slot layout (head gh).  Slots are read eight at a time (all
+    // eight reads in flight) and folded against a running maximum; the
     // batches and the order within them depend on kk alone.
     auto merge_slots = [&](int p0, int kk, int stride, int e, int gh, float& mx, float& den,
                            f32x4_t& num) {
@@ -326,18 +342,32 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         store_row4(row0 + gh, e, gh, num * (1.0f / den));
       }
     };
-    // Merges unit (b, hh)'s kk slots lu, lu + stride, ...: the output when the
-    // unit is whole in the window, else its piece, published to slot u + x.
-    auto merge_unit = [&](int lu, int kk, int stride, int whole, int b, int hh) {
+    // Merges the unit in entry ui, whose chunks are all folded and, when it
+    // has more than one batch, whose batches are merged into their first slots:
+    // the output when the unit is whole in the window; else its piece,
+    // published to workspace slot u + x and counted, and when it is the last
+    // of the unit's pieces to be counted, the merge of all of them.
+    auto finish_unit = [&](int ui) {
+      const int* ue = s_unit + ui * kUnitWords;
+      const int e0 = __builtin_amdgcn_readfirstlane(ue[0]);
+      const int lu = e0 & 4095;
+      const int kk = (e0 >> 12) & 4095;
+      const int whole = e0 >> 24;
+      const int b = __builtin_amdgcn_readfirstlane(ue[1]);
+      const int hh = __builtin_amdgcn_readfirstlane(ue[2]);
       const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hh) * G;
       const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
       float* pacc = prm.part_out + (u + x) * G * D;  // [G][16][NT]
       float* pml = prm.part_ml + (u + x) * G * 2;    // [G][max, sum]
+      const int nbat = (kk + kBatch - 1) / kBatch;
       for (int e = lane; e < G * E4; e += 64) {
         const int gh = e / E4;
         float mx, den;
         f32x4_t num;
-        merge_slots(lu, kk, stride, e, gh, mx, den, num);
+        if (nbat > 1)
+          merge_slots(lu, nbat, kBatch, e, gh, mx, den, num);  // the batches' first slots
+        else
+          merge_slots(lu, kk, 1, e, gh, mx, den, num);
         if (whole) {
           store_row4(row0 + gh, e, gh, num * (1.0f / den));
         } else {
@@ -348,6 +378,23 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
             store_coherent(pml + gh * 2 + 1, den);
           }
         }
+      }
+      if (whole) return;
+      // The piece's device-coherent stores have completed before it is
+      // counted (this waits for the wavefront's loads in flight as well).
+      __builtin_amdgcn_s_waitcnt(0);
+      uint32_t prev = 0;
+      if (lane == 0)
+        prev = __hip_atomic_fetch_add(prm.counters + u, 1u, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      prev = __builtin_amdgcn_readfirstlane(prev);
+      int64_t gf, gl;
+      unit_span(b, hh, gf, gl);
+      if (prev == static_cast<uint32_t>(gl - gf)) {
+        merge_pieces(b, hh, gf, gl);
+        // every piece has been counted: leave the counter at zero for the next call
+        if (lane == 0)
+          __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     };
     // A fused step's new token of the chunk in `sl8`, if it holds one, into
@@ -392,6 +439,57 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
       if (c == 0 && r < G) sm[r * 2] = st.m2;
     };
+    // Counts the chunk folded into slot `pos` in its batch; the wavefront
+    // that counts a batch's last chunk merges the batch into its first slot
+    // (units of one batch are merged from their slots at the end).
+    auto count = [&](int pos) {
+      const int fk = __builtin_amdgcn_readfirstlane(s_rec[pos * DS + 2]);
+      const int first = fk & 4095;
+      const int kk = fk >> 12;
+      if (kk <= kBatch) return;
+      const int bfirst = first + ((pos - first) & ~(kBatch - 1));
+      const int bsize = min(kBatch, first + kk - bfirst);
+      lds_release();
+      int done = 0;
+      if (lane == 0)
+        done = __hip_atomic_fetch_add(s_rec + bfirst * DS + 4, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP) + 1;
+      done = __builtin_amdgcn_readfirstlane(done);
+      lds_acquire();
+      if (done != bsize) return;
+      // Straight-line code (no loop with a run-time trip count): inside the
+      // streaming loop such a loop costs the compiler its exact count of the
+      // loads in flight, and every fold would then wait for all of them.
+#pragma unroll
+      for (int it = 0; it < kMaxIt; ++it) {
+        const int e = lane + 64 * it;
+        if (e < G * E4) {
+          const int gh = e / E4;
+          float2 ml[kBatch];
+          f32x4_t a[kBatch];
+#pragma unroll
+          for (int t = 0; t < kBatch; ++t) {
+            const int p = bfirst + min(t, bsize - 1);
+            ml[t] = *reinterpret_cast<const float2*>(s_ml + (p * G + gh) * 2);
+            a[t] = *reinterpret_cast<const f32x4_t*>(s_acc + static_cast<size_t>(p) * G * D + 4 * e);
+          }
+          float mx = ml[0].x;
+#pragma unroll
+          for (int t = 1; t < kBatch; ++t) mx = (t < bsize) ? fmaxf(mx, ml[t].x) : mx;
+          float den = 0.f;
+          f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < kBatch; ++t) {
+            const float f = (t < bsize) ? fast_exp2(ml[t].x - mx) : 0.f;
+            den += f * ml[t].y;
+            num += f * a[t];
+          }
+          *reinterpret_cast<f32x4_t*>(s_acc + static_cast<size_t>(bfirst) * G * D + 4 * e) = num;
+          if (e == gh * E4)
+            *reinterpret_cast<float2*>(s_ml + (bfirst * G + gh) * 2) = make_float2(mx, den);
+        }
+      }
+    };
 
     // 3. The wavefronts take chunks until the window's are gone.  Every ring
     // refill issues its loads (a chunk past the window re-reads the window's
@@ -407,12 +505,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     // A wavefront's grabs rise, and it folds its chunks in grab order: once
     // one lies past the window, so do all the ring's later entries.  (The
     // ring is walked with constant indices so its registers stay put.)
-    // After each fold the next chunk's new token (if it holds one) is
-    // loaded before the refill, so the fold that needs it waits for nothing
-    // else.
+    // After each fold the chunk is counted in its batch (and a batch it
+    // completes merged), then the next chunk's new token (if it holds one)
+    // is loaded before the refill, so the fold that needs it waits for
+    // nothing else.  The refill's loads are the last thing in the loop body:
+    // code after them leaves the compiler unable to count the loads in
+    // flight at the next fold, which then waits for all of them.
     static_assert(DEPTH >= 2 && DEPTH <= 3, "ring depth");
     auto advance = [&](Slot& sl8, int& j, const Slot& next) {
+      const int pos = sl8.pos;
       consume(sl8);
+      count(pos);
       load_new(next);
       j = grab();
       issue(j < n ? j : 0, sl8);
@@ -428,84 +531,20 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
     }
 
-    // 4. Every chunk of the window is in its slot.  Stage 1: every merge
-    // task (kBatch consecutive slots of one unit) is merged in place into the
-    // task's first slot, the tasks spread over all wavefronts.  Stage 2: the
-    // owner of each unit merges its batches (or, for a unit of at most kBatch
-    // chunks here, its slots).  The window's first and last units - the
-    // only ones a window edge can cut - have wavefronts 0 and NW - 1 to
-    // themselves; the others are dealt round robin to the rest.  A cut
-    // unit's piece is published, then counted, and the last piece of each
-    // unit merges them all.  Which wavefront merges what never changes a
-    // result bit: every merge order depends on the unit's chunk count alone.
+    // 4. Every chunk of the window is folded and every batch merged.  Each
+    // unit is merged by one wavefront: the first unit by wavefront 0, the
+    // last by wavefront NW - 1, the others round robin over the rest.
     __syncthreads();
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    {
-      const int ntask = __builtin_amdgcn_readfirstlane(s_misc[2]);
-      for (int i = w; i < ntask; i += NW) {
-        const int tk = __builtin_amdgcn_readfirstlane(s_task[i]);
-        const int pos = tk & 4095;
-        const int cnt = tk >> 12;
-        for (int e = lane; e < G * E4; e += 64) {
-          const int gh = e / E4;
-          float mx, den;
-          f32x4_t num;
-          merge_slots(pos, cnt, 1, e, gh, mx, den, num);
-          *reinterpret_cast<f32x4_t*>(s_acc + static_cast<size_t>(pos) * G * D + 4 * e) = num;
-          if (e == gh * E4)
-            *reinterpret_cast<float2*>(s_ml + (pos * G + gh) * 2) = make_float2(mx, den);
-        }
-      }
-      if (ntask > 0) __syncthreads();  // (ntask is the same in every wavefront)
-    }
-    int npub = 0, pub_b = 0, pub_h = 0;
-    auto own_unit = [&](int i) {
-      const int* ue = s_unit + i * kUnitWords;
-      const int e0 = __builtin_amdgcn_readfirstlane(ue[0]);
-      const int kk = (e0 >> 12) & 4095;
-      if (kk == 0) return;  // no last unit apart from the first
-      const int lu = e0 & 4095;
-      const int whole = e0 >> 24;
-      const int b = __builtin_amdgcn_readfirstlane(ue[1]);
-      const int hh = __builtin_amdgcn_readfirstlane(ue[2]);
-      if (kk > kBatch)
-        merge_unit(lu, (kk + kBatch - 1) / kBatch, kBatch, whole, b, hh);
-      else
-        merge_unit(lu, kk, 1, whole, b, hh);
-      if (!whole) {
-        pub_b = b;
-        pub_h = hh;
-        npub = 1;
-      }
-    };
     if (w == 0) {
-      own_unit(0);
+      finish_unit(0);
     } else if (w == NW - 1) {
-      own_unit(1);
+      // (a window holding one unit has no entry 1: its last chunk is unit 0's)
+      if ((__builtin_amdgcn_readfirstlane(s_rec[(n - 1) * DS + 3]) >> 12) == 1) finish_unit(1);
     } else {
-      const int nlist = 2 + __builtin_amdgcn_readfirstlane(s_misc[1]);
-      for (int i = 1 + w; i < nlist; i += NW - 2) own_unit(i);
-    }
-    if (npub > 0) {
-      __builtin_amdgcn_s_waitcnt(0);  // the piece is visible before it is counted
-      {
-        const int b = pub_b;
-        const int hh = pub_h;
-        const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
-        uint32_t prev = 0;
-        if (lane == 0)
-          prev = __hip_atomic_fetch_add(prm.counters + u, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-        prev = __builtin_amdgcn_readfirstlane(prev);
-        int64_t gf, gl;
-        unit_span(b, hh, gf, gl);
-        if (prev == static_cast<uint32_t>(gl - gf)) {
-          merge_pieces(b, hh, gf, gl);
-          // every piece has been counted: leave the counter at zero for the next call
-          if (lane == 0)
-            __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+      const int nlist = __builtin_amdgcn_readfirstlane(s_misc[3]);
+      for (int i = w - 1; i < nlist; i += NW - 2)
+        finish_unit(__builtin_amdgcn_readfirstlane(s_list[i]));
     }
   }
   if (fused && gwave < units) tw.store(prm, lane);
@@ -581,7 +620,7 @@ WgLayout wg_layout(int head_dim, int block_size, int group, int num_seqs, int ma
   w = up4(w + cap * (kRecBase + nb));
   lay.off_unit = w;
   w = up4(w + (cap + 2) * kUnitWords);
-  lay.off_task = w;
+  lay.off_list = w;
   w = up4(w + cap);
   lay.off_acc = w;
   w = up4(w + cap * group * head_dim);

@@ -83,7 +83,7 @@ constexpr int kWgMaxCapacity = 1024;     // chunks a window holds at most
 struct WgLayout {
   int32_t capacity;     // chunks per window
   int32_t max_windows;  // windows per workgroup the workspace has slots for
-  int32_t off_len, off_pre, off_wsum, off_misc, off_rec, off_unit, off_task, off_acc, off_ml;
+  int32_t off_len, off_pre, off_wsum, off_misc, off_rec, off_unit, off_list, off_acc, off_ml;
   int32_t words;        // total LDS words
 };
 int wg_waves_per_group(int head_dim);
