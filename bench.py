@@ -222,6 +222,7 @@ def read_ceiling(pkv, torch, dev, stream, kv_bytes: int, launches: int) -> dict:
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    prime(stream)
     e0.record(stream)
     for r in range(launches):
         read_probe(src, orders[r % regions], sink)
@@ -233,6 +234,18 @@ def read_ceiling(pkv, torch, dev, stream, kv_bytes: int, launches: int) -> dict:
             "us_per_launch": round(ms * 1e3, 3), "bytes": tiles * 2048,
             "kind": "trivial read kernel (libpkv_probe.so): the step's byte count as 2 KiB "
                     "tiles in random order, 8 rotated regions, launches back to back"}
+
+
+def prime(stream) -> None:
+    """Hold `stream` with a short GPU-side sleep before a timed region opens,
+    so that the host has enqueued the region's first steps by the time the
+    start event runs: otherwise the GPU idles for the host's per-call cost of
+    the first step inside every timed region (~13 us here, about 0.65 us per
+    step over 20 steps)."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(2_000_000)
 
 
 def timed_graph(fn, calls: int, replays: int = 10) -> float:
@@ -275,6 +288,7 @@ def timed(stream, fn, launches: int, warmup: int = 3) -> float:
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    prime(stream)
     e0.record(stream)
     for i in range(launches):
         fn(warmup + i)
@@ -703,14 +717,17 @@ def main() -> int:
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
 
     # Each timed region: K steps back to back between one pair of events on
-    # the stream the kernels run on, synchronised on both sides.  The value is
-    # the median over the trials.
+    # the stream the kernels run on, synchronised on both sides; the stream
+    # is held by a short GPU sleep before the start event, so the host has
+    # the first steps enqueued when the region opens.  The value is the
+    # median over the trials.
     trial_ms = []
     nxt = args.warmup
     for _ in range(max(args.trials, 1)):
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        prime(stream)
         t_start.record(stream)
         for i in range(args.steps):
             step(nxt + i)

@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   };
 
   // Sequence holding global chunk cc: the largest lo with Hkv * s_pre[lo] <= cc.
-  auto seq_of = [&](int64_t cc) {
+  auto seq_of = [&](int64_t cc) __attribute__((always_inline)) {
     int lo = 0, hi = S;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     return lo;
   };
   // Unit of global chunk cc and the chunk's index in it.
-  auto locate = [&](int64_t cc, int& b, int& h, int& lc) {
+  auto locate = [&](int64_t cc, int& b, int& h, int& lc) __attribute__((always_inline)) {
     b = seq_of(cc);
     const int nb = (s_len[b] + 31) >> 5;
     const int rem = static_cast<int>(cc - static_cast<int64_t>(Hkv) * s_pre[b]);
@@ -230,20 +230,20 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       __syncthreads();
     }
     // Windows holding the first and the last chunk of unit (b, h).
-    auto unit_span = [&](int b, int h, int64_t& gf, int64_t& gl) {
+    auto unit_span = [&](int b, int h, int64_t& gf, int64_t& gl) __attribute__((always_inline)) {
       const int nb = (s_len[b] + 31) >> 5;
       const int64_t cu0 = static_cast<int64_t>(Hkv) * s_pre[b] + static_cast<int64_t>(h) * nb;
       gf = ((cu0 + 1) * NWeff - 1) / C;
       gl = ((cu0 + nb) * NWeff - 1) / C;
     };
 
-    auto grab = [&]() {
+    auto grab = [&]() __attribute__((always_inline)) {
       int j = 0;
       if (lane == 0)
         j = __hip_atomic_fetch_add(s_misc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       return __builtin_amdgcn_readfirstlane(j);
     };
-    auto issue = [&](int pos, Slot& sl8) {
+    auto issue = [&](int pos, Slot& sl8) __attribute__((always_inline)) {
       const int* rec = s_rec + pos * DS;
       const int b = __builtin_amdgcn_readfirstlane(rec[0]);
       const int hh = __builtin_amdgcn_readfirstlane(rec[1]);
@@ -263,7 +263,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     // eight reads in flight) and folded against a running maximum; the
     // batches and the order within them depend on kk alone.
     auto merge_slots = [&](int p0, int kk, int stride, int e, int gh, float& mx, float& den,
-                           f32x4_t& num) {
+                           f32x4_t& num) __attribute__((always_inline)) {
       mx = -INFINITY;
       den = 0.f;
       num = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -295,7 +295,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
     };
     // Output row features of float4 e: d = 16 nt + rr for nt = 4 n4 .. 4 n4 + 3.
-    auto store_row4 = [&](size_t row, int e, int gh, const f32x4_t& v) {
+    auto store_row4 = [&](size_t row, int e, int gh, const f32x4_t& v) __attribute__((always_inline)) {
       const int rem = e - gh * E4;
       const int rr = rem / (NT / 4);
       const int n4 = rem - rr * (NT / 4);
@@ -303,9 +303,100 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       for (int t = 0; t < 4; ++t)
         store_out(prm.out, row * D + 16 * (4 * n4 + t) + rr, v[t], prm.out_f32);
     };
-    // All pieces of unit (b, hh) - windows gf .. gl, published and counted -
-    // merged in window order into the output.
-    auto merge_pieces = [&](int b, int hh, int64_t gf, int64_t gl) {
+    // Counts the chunk folded into slot `pos`: in its unit when the unit has
+    // at most one batch here, else in its batch, and the wavefront that
+    // counts a batch's last chunk merges the batch into its first slot and
+    // counts the batch in the unit.  A unit is complete when its count
+    // reaches unit_target.
+    auto count = [&](int pos) __attribute__((always_inline)) {
+      const int* rec = s_rec + pos * DS;
+      const int fk = __builtin_amdgcn_readfirstlane(rec[2]);
+      const int ui = (__builtin_amdgcn_readfirstlane(rec[3]) >> 12) & 4095;
+      const int first = fk & 4095;
+      const int kk = fk >> 12;
+      if (kk > kBatch) {
+        const int bfirst = first + ((pos - first) & ~(kBatch - 1));
+        const int bsize = min(kBatch, first + kk - bfirst);
+        lds_release();
+        int done = 0;
+        if (lane == 0)
+          done = __hip_atomic_fetch_add(s_rec + bfirst * DS + 4, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_WORKGROUP) + 1;
+        done = __builtin_amdgcn_readfirstlane(done);
+        lds_acquire();
+        if (done != bsize) return;
+        // Straight-line code (no loop with a run-time trip count): inside the
+        // streaming loop such a loop costs the compiler its exact count of the
+        // loads in flight, and every fold would then wait for all of them.
+#pragma unroll
+        for (int it = 0; it < kMaxIt; ++it) {
+          const int e = lane + 64 * it;
+          if (e < G * E4) {
+            const int gh = e / E4;
+            float2 ml[kBatch];
+            f32x4_t a[kBatch];
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) {
+              const int p = bfirst + min(t, bsize - 1);
+              ml[t] = *reinterpret_cast<const float2*>(s_ml + (p * G + gh) * 2);
+              a[t] = *reinterpret_cast<const f32x4_t*>(s_acc + static_cast<size_t>(p) * G * D + 4 * e);
+            }
+            float mx = ml[0].x;
+#pragma unroll
+            for (int t = 1; t < kBatch; ++t) mx = (t < bsize) ? fmaxf(mx, ml[t].x) : mx;
+            float den = 0.f;
+            f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) {
+              const float f = (t < bsize) ? fast_exp2(ml[t].x - mx) : 0.f;
+              den += f * ml[t].y;
+              num += f * a[t];
+            }
+            *reinterpret_cast<f32x4_t*>(s_acc + static_cast<size_t>(bfirst) * G * D + 4 * e) = num;
+            if (e == gh * E4)
+              *reinterpret_cast<float2*>(s_ml + (bfirst * G + gh) * 2) = make_float2(mx, den);
+          }
+        }
+      }
+      lds_release();
+      if (lane == 0)
+        __hip_atomic_fetch_add(s_unit + ui * kUnitWords + 3, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto unit_target = [&](int ui) __attribute__((always_inline)) {
+      const int kk = (__builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords]) >> 12) & 4095;
+      return kk <= kBatch ? kk : (kk + kBatch - 1) / kBatch;
+    };
+    auto unit_count = [&](int ui) __attribute__((always_inline)) {
+      return __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+          s_unit + ui * kUnitWords + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    };
+    // Waits until every chunk of the unit in entry ui is folded and counted.
+    // Only a wavefront that has folded all of its own chunks waits, so the
+    // chunks it waits for are in the hands of wavefronts still folding.
+    auto wait_unit = [&](int ui) __attribute__((always_inline)) {
+      const int target = unit_target(ui);
+      while (unit_count(ui) != target) __builtin_amdgcn_s_sleep(1);
+      lds_acquire();
+    };
+
+    // The window's own state of the unit in entry ui (complete) for float4 e:
+    // its batches' merged slots, or its chunks' slots for a one-batch unit.
+    auto own_state = [&](int ui, int e, int gh, float& mx, float& den, f32x4_t& num) __attribute__((always_inline)) {
+      const int e0 = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords]);
+      const int lu = e0 & 4095;
+      const int kk = (e0 >> 12) & 4095;
+      if (kk > kBatch)
+        merge_slots(lu, (kk + kBatch - 1) / kBatch, kBatch, e, gh, mx, den, num);
+      else
+        merge_slots(lu, kk, 1, e, gh, mx, den, num);
+    };
+    // Every piece of unit (b, hh) - windows gf .. gl - merged in window order
+    // into the output.  Piece own_j, when own_j >= 0, is this window's and is
+    // taken from its slots (entry own_ui) instead of the workspace; the others
+    // are published and counted.  The arithmetic is the same either way, so
+    // the result does not depend on which window merges.
+    auto merge_pieces = [&](int b, int hh, int64_t gf, int64_t gl, int own_j, int own_ui) __attribute__((always_inline)) {
       const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
       const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hh) * G;
       const int kp = static_cast<int>(gl - gf + 1);
@@ -315,6 +406,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
                                static_cast<uint32_t>(kp * G * 2 * sizeof(float)));
       for (int e = lane; e < G * E4; e += 64) {
         const int gh = e / E4;
+        float omx = 0.f, oden = 0.f;
+        f32x4_t onum = {0.f, 0.f, 0.f, 0.f};
+        if (own_j >= 0) own_state(own_ui, e, gh, omx, oden, onum);
         float mx = -INFINITY, den = 0.f;
         f32x4_t num = {0.f, 0.f, 0.f, 0.f};
         for (int j0 = 0; j0 < kp; j0 += 8) {  // eight pieces' loads in flight at a time
@@ -330,11 +424,15 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             if (j0 + t < kp) {
-              const float mn = fmaxf(mx, pm[t]);
+              const bool mine = j0 + t == own_j;
+              const float pmt = mine ? omx : pm[t];
+              const float plt = mine ? oden : pl[t];
+              const f32x4_t at = mine ? onum : a[t];
+              const float mn = fmaxf(mx, pmt);
               const float fo = fast_exp2(mx - mn);  // 0 for the first piece
-              const float fj = fast_exp2(pm[t] - mn);
-              den = den * fo + pl[t] * fj;
-              num = num * fo + a[t] * fj;
+              const float fj = fast_exp2(pmt - mn);
+              den = den * fo + plt * fj;
+              num = num * fo + at * fj;
               mx = mn;
             }
           }
@@ -342,44 +440,42 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         store_row4(row0 + gh, e, gh, num * (1.0f / den));
       }
     };
-    // Merges the unit in entry ui, whose chunks are all folded and, when it
-    // has more than one batch, whose batches are merged into their first slots:
-    // the output when the unit is whole in the window; else its piece,
-    // published to workspace slot u + x and counted, and when it is the last
-    // of the unit's pieces to be counted, the merge of all of them.
-    auto finish_unit = [&](int ui) {
-      const int* ue = s_unit + ui * kUnitWords;
-      const int e0 = __builtin_amdgcn_readfirstlane(ue[0]);
-      const int lu = e0 & 4095;
-      const int kk = (e0 >> 12) & 4095;
-      const int whole = e0 >> 24;
-      const int b = __builtin_amdgcn_readfirstlane(ue[1]);
-      const int hh = __builtin_amdgcn_readfirstlane(ue[2]);
+    // A whole unit (entry ui, complete) to the output.
+    auto finish_whole = [&](int ui) __attribute__((always_inline)) {
+      const int b = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 1]);
+      const int hh = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 2]);
       const size_t row0 = static_cast<size_t>(b) * Hq + static_cast<size_t>(hh) * G;
-      const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
-      float* pacc = prm.part_out + (u + x) * G * D;  // [G][16][NT]
-      float* pml = prm.part_ml + (u + x) * G * 2;    // [G][max, sum]
-      const int nbat = (kk + kBatch - 1) / kBatch;
       for (int e = lane; e < G * E4; e += 64) {
         const int gh = e / E4;
         float mx, den;
         f32x4_t num;
-        if (nbat > 1)
-          merge_slots(lu, nbat, kBatch, e, gh, mx, den, num);  // the batches' first slots
-        else
-          merge_slots(lu, kk, 1, e, gh, mx, den, num);
-        if (whole) {
-          store_row4(row0 + gh, e, gh, num * (1.0f / den));
-        } else {
+        own_state(ui, e, gh, mx, den, num);
+        store_row4(row0 + gh, e, gh, num * (1.0f / den));
+      }
+    };
+    // Publishes this window's piece of the cut unit in entry ui (complete) to
+    // workspace slot u + x and counts it; true when it was the last of the
+    // unit's pieces to be counted.
+    auto publish = [&](int ui) __attribute__((always_inline)) {
+      const int b = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 1]);
+      const int hh = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 2]);
+      const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
+      int64_t gf, gl;
+      unit_span(b, hh, gf, gl);
+      float* pacc = prm.part_out + (u + x) * G * D;  // [G][16][NT]
+      float* pml = prm.part_ml + (u + x) * G * 2;    // [G][max, sum]
+      for (int e = lane; e < G * E4; e += 64) {
+        const int gh = e / E4;
+        float mx, den;
+        f32x4_t num;
+        own_state(ui, e, gh, mx, den, num);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) store_coherent(pacc + 4 * e + t, num[t]);
-          if (e == gh * E4) {
-            store_coherent(pml + gh * 2, mx);
-            store_coherent(pml + gh * 2 + 1, den);
-          }
+        for (int t = 0; t < 4; ++t) store_coherent(pacc + 4 * e + t, num[t]);
+        if (e == gh * E4) {
+          store_coherent(pml + gh * 2, mx);
+          store_coherent(pml + gh * 2 + 1, den);
         }
       }
-      if (whole) return;
       // The piece's device-coherent stores have completed before it is
       // counted (this waits for the wavefront's loads in flight as well).
       __builtin_amdgcn_s_waitcnt(0);
@@ -388,18 +484,57 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         prev = __hip_atomic_fetch_add(prm.counters + u, 1u, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
       prev = __builtin_amdgcn_readfirstlane(prev);
+      return prev == static_cast<uint32_t>(gl - gf);
+    };
+    // After the last piece of the cut unit in entry ui was counted here: all
+    // pieces merged into the output, and the counter left at zero for the
+    // next call.
+    auto merge_all = [&](int ui) __attribute__((always_inline)) {
+      const int b = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 1]);
+      const int hh = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 2]);
+      const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
       int64_t gf, gl;
       unit_span(b, hh, gf, gl);
-      if (prev == static_cast<uint32_t>(gl - gf)) {
-        merge_pieces(b, hh, gf, gl);
-        // every piece has been counted: leave the counter at zero for the next call
-        if (lane == 0)
-          __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __asm__ __volatile__("" ::: "memory");
+      merge_pieces(b, hh, gf, gl, -1, ui);
+      if (lane == 0)
+        __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // A cut unit (entry ui, waited for here): this window's piece is published to
+    // workspace slot u + x and counted; when it is the last of the unit's
+    // pieces to be counted, all of them are merged into the output.  With
+    // `fast`, the counter is read first: when every other piece is counted
+    // already, they are merged with this window's state straight away and
+    // nothing is published (the counter is then left at zero for the next
+    // call; no other window touches it again).
+    auto finish_cut = [&](int ui, bool fast) __attribute__((always_inline)) {
+      const int b = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 1]);
+      const int hh = __builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords + 2]);
+      const int64_t u = static_cast<int64_t>(b) * Hkv + hh;
+      int64_t gf, gl;
+      unit_span(b, hh, gf, gl);
+      const uint32_t others = static_cast<uint32_t>(gl - gf);
+      uint32_t seen = 0;
+      if (fast && lane == 0)
+        seen = __hip_atomic_load(prm.counters + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_unit(ui);
+      if (fast) {
+        seen = __builtin_amdgcn_readfirstlane(seen);
+        if (seen == others) {
+          // The other pieces were stored and acknowledged before they were
+          // counted, and their loads are issued after the count was seen.
+          __asm__ __volatile__("" ::: "memory");
+          merge_pieces(b, hh, gf, gl, static_cast<int>(x - gf), ui);
+          if (lane == 0)
+            __hip_atomic_store(prm.counters + u, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          return;
+        }
       }
+      if (publish(ui)) merge_all(ui);
     };
     // A fused step's new token of the chunk in `sl8`, if it holds one, into
     // `nxt` (the chunk is the next one this wavefront folds).
-    auto load_new = [&](const Slot& sl8) {
+    auto load_new = [&](const Slot& sl8) __attribute__((always_inline)) {
       const int* rec = s_rec + sl8.pos * DS;
       const int vf = __builtin_amdgcn_readfirstlane(rec[3]);
       if (((vf >> 8) & 4) && prm.k_new != nullptr) {
@@ -410,7 +545,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
     };
     // Folds the chunk in `sl8` into its LDS slot.
-    auto consume = [&](Slot& sl8) {
+    auto consume = [&](Slot& sl8) __attribute__((always_inline)) {
       const int pos = sl8.pos;
       const int* rec = s_rec + pos * DS;
       const int vf = __builtin_amdgcn_readfirstlane(rec[3]);
@@ -439,80 +574,30 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       }
       if (c == 0 && r < G) sm[r * 2] = st.m2;
     };
-    // Counts the chunk folded into slot `pos` in its batch; the wavefront
-    // that counts a batch's last chunk merges the batch into its first slot
-    // (units of one batch are merged from their slots at the end).
-    auto count = [&](int pos) {
-      const int fk = __builtin_amdgcn_readfirstlane(s_rec[pos * DS + 2]);
-      const int first = fk & 4095;
-      const int kk = fk >> 12;
-      if (kk <= kBatch) return;
-      const int bfirst = first + ((pos - first) & ~(kBatch - 1));
-      const int bsize = min(kBatch, first + kk - bfirst);
-      lds_release();
-      int done = 0;
-      if (lane == 0)
-        done = __hip_atomic_fetch_add(s_rec + bfirst * DS + 4, 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_WORKGROUP) + 1;
-      done = __builtin_amdgcn_readfirstlane(done);
-      lds_acquire();
-      if (done != bsize) return;
-      // Straight-line code (no loop with a run-time trip count): inside the
-      // streaming loop such a loop costs the compiler its exact count of the
-      // loads in flight, and every fold would then wait for all of them.
-#pragma unroll
-      for (int it = 0; it < kMaxIt; ++it) {
-        const int e = lane + 64 * it;
-        if (e < G * E4) {
-          const int gh = e / E4;
-          float2 ml[kBatch];
-          f32x4_t a[kBatch];
-#pragma unroll
-          for (int t = 0; t < kBatch; ++t) {
-            const int p = bfirst + min(t, bsize - 1);
-            ml[t] = *reinterpret_cast<const float2*>(s_ml + (p * G + gh) * 2);
-            a[t] = *reinterpret_cast<const f32x4_t*>(s_acc + static_cast<size_t>(p) * G * D + 4 * e);
-          }
-          float mx = ml[0].x;
-#pragma unroll
-          for (int t = 1; t < kBatch; ++t) mx = (t < bsize) ? fmaxf(mx, ml[t].x) : mx;
-          float den = 0.f;
-          f32x4_t num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int t = 0; t < kBatch; ++t) {
-            const float f = (t < bsize) ? fast_exp2(ml[t].x - mx) : 0.f;
-            den += f * ml[t].y;
-            num += f * a[t];
-          }
-          *reinterpret_cast<f32x4_t*>(s_acc + static_cast<size_t>(bfirst) * G * D + 4 * e) = num;
-          if (e == gh * E4)
-            *reinterpret_cast<float2*>(s_ml + (bfirst * G + gh) * 2) = make_float2(mx, den);
-        }
-      }
-    };
-
     // 3. The wavefronts take chunks until the window's are gone.  Every ring
     // refill issues its loads (a chunk past the window re-reads the window's
     // first chunk, which nobody folds) so the wait counts stay exact.
-    Slot ring[DEPTH];
-    int jr[DEPTH];
+    static_assert(DEPTH == 2, "ring depth");
+    Slot ring[2];
+    int jr[2];
 #pragma unroll
-    for (int s = 0; s < DEPTH; ++s) {
+    for (int s = 0; s < 2; ++s) {
       jr[s] = grab();
       issue(jr[s] < n ? jr[s] : 0, ring[s]);
       if (s == 0) load_new(ring[0]);
     }
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     // A wavefront's grabs rise, and it folds its chunks in grab order: once
     // one lies past the window, so do all the ring's later entries.  (The
     // ring is walked with constant indices so its registers stay put.)
-    // After each fold the chunk is counted in its batch (and a batch it
-    // completes merged), then the next chunk's new token (if it holds one)
-    // is loaded before the refill, so the fold that needs it waits for
-    // nothing else.  The refill's loads are the last thing in the loop body:
-    // code after them leaves the compiler unable to count the loads in
-    // flight at the next fold, which then waits for all of them.
-    static_assert(DEPTH >= 2 && DEPTH <= 3, "ring depth");
-    auto advance = [&](Slot& sl8, int& j, const Slot& next) {
+    // After each fold the chunk is counted (and a batch it completes
+    // merged), then the next chunk's new token (if it holds one) is loaded
+    // before the refill, so the fold that needs it waits for nothing else.
+    // The refill's loads are the last thing in the loop body: code after
+    // them, or a global store or atomic anywhere in the loop, leaves the
+    // compiler unable to count the loads in flight at the next fold, which
+    // then waits for all of them.
+    auto advance = [&](Slot& sl8, int& j, const Slot& next) __attribute__((always_inline)) {
       const int pos = sl8.pos;
       consume(sl8);
       count(pos);
@@ -524,27 +609,34 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       if (jr[0] >= n) break;
       advance(ring[0], jr[0], ring[1]);
       if (jr[1] >= n) break;
-      advance(ring[1], jr[1], ring[DEPTH > 2 ? 2 : 0]);
-      if constexpr (DEPTH > 2) {
-        if (jr[2] >= n) break;
-        advance(ring[2], jr[2], ring[0]);
-      }
+      advance(ring[1], jr[1], ring[0]);
     }
 
-    // 4. Every chunk of the window is folded and every batch merged.  Each
-    // unit is merged by one wavefront: the first unit by wavefront 0, the
-    // last by wavefront NW - 1, the others round robin over the rest.
-    __syncthreads();
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // 4. Each unit is finished by one wavefront as soon as it is complete
+    // (the others may still be folding; no barrier): the first unit by
+    // wavefront 0, the last by wavefront NW - 1, the others round robin over
+    // the rest.  The first unit's chunks come first in the window, so
+    // wavefront 0 usually publishes its piece while the window's last chunks
+    // are still being folded.  A cut unit's owner reads the unit's counter
+    // while it waits for the unit's last chunks, and when every other piece
+    // is counted already, merges them without publishing its own.
+    auto finish = [&](int ui) __attribute__((always_inline)) {
+      if ((__builtin_amdgcn_readfirstlane(s_unit[ui * kUnitWords]) >> 24) != 0) {
+        wait_unit(ui);
+        finish_whole(ui);
+      } else {
+        finish_cut(ui, true);
+      }
+    };
     if (w == 0) {
-      finish_unit(0);
+      finish(0);
     } else if (w == NW - 1) {
       // (a window holding one unit has no entry 1: its last chunk is unit 0's)
-      if ((__builtin_amdgcn_readfirstlane(s_rec[(n - 1) * DS + 3]) >> 12) == 1) finish_unit(1);
+      if ((__builtin_amdgcn_readfirstlane(s_rec[(n - 1) * DS + 3]) >> 12) == 1) finish(1);
     } else {
       const int nlist = __builtin_amdgcn_readfirstlane(s_misc[3]);
       for (int i = w - 1; i < nlist; i += NW - 2)
-        finish_unit(__builtin_amdgcn_readfirstlane(s_list[i]));
+        finish(__builtin_amdgcn_readfirstlane(s_list[i]));
     }
   }
   if (fused && gwave < units) tw.store(prm, lane);
