@@ -687,7 +687,12 @@ hipError_t launch_wg_bs(const DecodeLaunch& a, int groups, const WgLayout& lay, 
 
 }  // namespace
 
-int wg_waves_per_group(int head_dim) { return head_dim <= 64 ? 8 : 4; }
+// Wavefronts per workgroup: at head_dim 64, six (two SIMDs with two, two
+// with one): measured against four to eight on the Llama-shaped batch of 64
+// (31.9 us against 32.5 us for eight, 32.0-32.5 us for four, five and
+// seven).  More bytes in flight per compute unit than six wavefronts hold
+// only lengthen the queues at the end of a window.  At head_dim 128, four.
+int wg_waves_per_group(int head_dim) { return head_dim <= 64 ? 6 : 4; }
 
 WgLayout wg_layout(int head_dim, int block_size, int group, int num_seqs, int max_windows) {
   WgLayout lay = {};
@@ -729,7 +734,7 @@ hipError_t launch_decode_wg(const DecodeLaunch& a, int num_groups, int max_windo
                                  max_windows);
   if (lay.capacity < 1) return hipErrorInvalidValue;
   const size_t lds = static_cast<size_t>(lay.words) * 4;
-  return a.prm.head_dim == 64 ? launch_wg_bs<64, 8>(a, num_groups, lay, lds, stream)
+  return a.prm.head_dim == 64 ? launch_wg_bs<64, 6>(a, num_groups, lay, lds, stream)
                               : launch_wg_bs<128, 4>(a, num_groups, lay, lds, stream);
 }
 
