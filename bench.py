@@ -16,10 +16,12 @@ total) that it cannot sit in the 256 MB Infinity Cache between steps.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
 ``--workload`` is llama_b64 (default, the headline line) or long_splitkv;
-prefix_cow, pool16, prefill_chunked and swap print their own report lines instead
-(logical and unique GB/s with the shared-prefix decode and the copy_blocks
-time; the 16-layer pool step per block size; the chunked prefill's matrix-core
-rate; block swap-out/in against the host link).
+prefix_cow, pool16, prefill_chunked, swap and size_sweep print their own report
+lines instead (logical and unique GB/s with the shared-prefix decode and the
+copy_blocks time; the 16-layer pool step per block size, fused and unfused
+writer; the chunked prefill's matrix-core rate; block swap-out/in against the
+host link; the llama-shaped step at 16 .. 256 sequences and the read kernel at
+32 MiB .. 1 GiB, each fitted to a fixed cost plus a streaming rate).
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this build runs on one
 GPU.  ``roofline.achieved`` is the decode launch alone (HIP events on the
@@ -83,18 +85,19 @@ def source_digest() -> str:
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per decode launch from the committed counter record, if it
+    """HBM bytes per decode launch from the committed counter records, if one
     was taken on this workload and kernel with the current decode source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            recs = json.load(f).get("records", [])
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("workload") != workload or rec.get("kernel") != kernel:
-        return None
-    if rec.get("decode_source_sha256") != source_digest():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    digest = source_digest()
+    for rec in recs:
+        if (rec.get("workload"), rec.get("kernel")) == (workload, kernel) \
+                and rec.get("decode_source_sha256") == digest:
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def calibrate_copy(mib: int, reps: int) -> int:
@@ -563,14 +566,24 @@ def run_pool16(args) -> int:
             layers.append((kc, vc, q))
         k_new, v_new = kt[lastd].contiguous(), vt[lastd].contiguous()
         del kt, vt
+        new_slots = torch.from_numpy(slots[last]).to(dev)
         out = torch.empty((S, hq, d), dtype=torch.bfloat16, device=dev)
         ws = pkv.DecodeWorkspace(device=dev)
-        kw = dict(max_seq_len=int(w.seq_lens.max()), kernel=args.kernel, workspace=ws)
+        # every block belongs to one sequence (the block manager hands each
+        # out once), which the calls may declare
+        no_shared = not args.plain_loads
+        kw = dict(max_seq_len=int(w.seq_lens.max()), kernel=args.kernel, workspace=ws,
+                  no_shared_blocks=no_shared)
 
         def step_append(i):
             for kc, vc, q in layers:
                 pkv.paged_attention_decode_append(q, k_new, v_new, kc, vc, bt, lens, bs, w.scale,
                                                   out, **kw)
+
+        def step_unfused(i):
+            for kc, vc, q in layers:
+                pkv.reshape_and_cache(k_new, v_new, new_slots, kc, vc)
+                pkv.paged_attention_decode(q, kc, vc, bt, lens, bs, w.scale, out, **kw)
 
         def step_decode(i):
             for kc, vc, q in layers:
@@ -578,19 +591,112 @@ def run_pool16(args) -> int:
 
         n = max(args.steps // 10, 5)
         ms_a = timed(stream, step_append, n, 2)
+        ms_u = timed(stream, step_unfused, n, 2)
         ms_d = timed(stream, step_decode, n, 2)
         per_layer = w.kv_bytes()
         res["by_block_size"][str(bs)] = {
             "kernel": pkv.decode_plan_kernel(layers[0][2], layers[0][0], bt,
-                                             max_seq_len=kw["max_seq_len"], kernel=args.kernel),
+                                             max_seq_len=kw["max_seq_len"], kernel=args.kernel,
+                                             no_shared_blocks=no_shared),
+            "no_shared_blocks": no_shared,
             "tokens_per_layer": w.total_tokens, "kv_bytes_per_layer": per_layer,
-            "step_ms_with_writer": round(ms_a, 4), "step_ms_without_writer": round(ms_d, 4),
+            "step_ms_with_writer": round(ms_a, 4),
+            "step_ms_writer_then_decode": round(ms_u, 4),
+            "step_ms_without_writer": round(ms_d, 4),
             "per_layer_gbs_with_writer": round(16 * per_layer / (ms_a * 1e-3) / 1e9, 1),
+            "per_layer_gbs_writer_then_decode": round(16 * per_layer / (ms_u * 1e-3) / 1e9, 1),
             "per_layer_gbs_without_writer": round(16 * per_layer / (ms_d * 1e-3) / 1e9, 1),
             "tokens_per_s": round(S / (ms_a * 1e-3), 1), "steps": n}
-        log(f"pool16 B={bs}: step {ms_a:.3f} ms with the writer, {ms_d:.3f} ms without")
+        log(f"pool16 B={bs}: step {ms_a:.3f} ms with the fused writer, {ms_u:.3f} ms with "
+            f"reshape_and_cache then decode, {ms_d:.3f} ms without a writer")
         del layers, out
         torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def run_size_sweep(args) -> int:
+    """Separates the decode step's fixed cost from its streaming rate: the
+    llama-shaped fused step (32 q / 8 KV heads, head_dim 64, block 16,
+    lengths U[128, 2048]) at S = 16 .. 256 sequences, and the trivial read
+    kernel over 32 MiB .. 1 GiB of 2 KiB tiles (random and sequential
+    order), each fitted with time = intercept + bytes / rate.  K/V values are
+    drawn on the device; regions rotate so that no launch reads a cache-
+    resident one."""
+    import torch
+
+    import paged_kv_cache_373_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    n = max(args.steps // 4, 20)
+    trials = max(args.trials, 3)
+
+    def med(fn):
+        return float(np.median([timed(stream, fn, n, 3) for _ in range(trials)])) * 1e3
+
+    def fit(rows):
+        x = np.array([r["bytes"] for r in rows], float)
+        y = np.array([r["us"] for r in rows], float)
+        slope, icpt = np.linalg.lstsq(np.vstack([x, np.ones_like(x)]).T, y, rcond=None)[0]
+        return {"intercept_us": round(float(icpt), 2), "rate_gbs": round(1e-3 / float(slope), 1)}
+
+    res = {"workload": "size_sweep", "steps_per_trial": n, "trials": trials}
+    dec = []
+    for S in (16, 32, 64, 128, 256):
+        w = workloads.llama_decode(num_seqs=S, with_kv=False)
+        hkv, d, bs = w.num_kv_heads, w.head_dim, w.block_size
+        pool_bytes = 2 * w.num_blocks * hkv * bs * d * 2
+        copies = max(2, math.ceil(ROTATE_BYTES / pool_bytes))
+        caches = []
+        for _ in range(copies):
+            kc, vc = pkv.new_kv_cache(w.num_blocks, hkv, bs, d, device=dev)
+            kc.normal_()
+            vc.normal_()
+            caches.append((kc, vc))
+        bt = torch.from_numpy(w.block_tables).to(dev)
+        lens = torch.from_numpy(w.seq_lens).to(dev)
+        q = torch.randn((S, w.num_q_heads, d), device=dev).to(torch.bfloat16)
+        kn = torch.randn((S, hkv, d), device=dev).to(torch.bfloat16)
+        vn = torch.randn((S, hkv, d), device=dev).to(torch.bfloat16)
+        out = torch.empty((S, w.num_q_heads, d), dtype=torch.bfloat16, device=dev)
+        kw = dict(max_seq_len=int(w.seq_lens.max()), workspace=pkv.DecodeWorkspace(device=dev),
+                  no_shared_blocks=not args.plain_loads)
+
+        def step(i):
+            kc, vc = caches[i % copies]
+            pkv.paged_attention_decode_append(q, kn, vn, kc, vc, bt, lens, bs, w.scale, out, **kw)
+
+        us = med(step)
+        kvb = w.kv_bytes()
+        dec.append({"num_seqs": S, "bytes": kvb, "us": round(us, 2),
+                    "gbs": round(kvb / us / 1e3, 1), "frac": round(kvb / us / 1e3 / HBM_PEAK_GBS, 4)})
+        log(f"decode S={S}: {kvb / 1e6:.1f} MB in {us:.2f} us ({kvb / us / 1e3:.0f} GB/s)")
+        del caches
+        torch.cuda.empty_cache()
+    res["decode_step"] = {"rows": dec, "fit": fit(dec)}
+    probe = {"random": [], "sequential": []}
+    g = torch.Generator().manual_seed(373)
+    for mib in (32, 64, 128, 256, 512, 1024):
+        tiles = (mib << 20) // 2048 // 32 * 32
+        regions = max(2, math.ceil(ROTATE_BYTES / (tiles * 2048)) + 1)
+        src = torch.zeros(regions * tiles * 2048, dtype=torch.uint8, device=dev)
+        sink = torch.empty(tiles * 8, dtype=torch.int32, device=dev)
+        orders = {"random": [(torch.randperm(tiles, generator=g) + r * tiles).to(torch.int32)
+                             .to(dev) for r in range(regions)],
+                  "sequential": [(torch.arange(tiles) + r * tiles).to(torch.int32).to(dev)
+                                 for r in range(regions)]}
+        for kind, ords in orders.items():
+            us = med(lambda i: read_probe(src, ords[i % regions], sink))
+            b = tiles * 2048
+            probe[kind].append({"mib": mib, "bytes": b, "us": round(us, 2),
+                                "gbs": round(b / us / 1e3, 1),
+                                "frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)})
+            log(f"read probe {kind} {mib} MiB: {us:.2f} us ({b / us / 1e3:.0f} GB/s)")
+        del src, sink, orders
+        torch.cuda.empty_cache()
+    res["read_probe"] = {k: {"rows": v, "fit": fit(v)} for k, v in probe.items()}
     print(json.dumps(res), flush=True)
     return 0
 
@@ -637,6 +743,8 @@ def main() -> int:
         return run_prefill(args)
     if args.workload == "swap":
         return run_swap(args)
+    if args.workload == "size_sweep":
+        return run_size_sweep(args)
 
     import torch
 

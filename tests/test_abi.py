@@ -122,13 +122,16 @@ def test_workspace_size_rules_stream():
 
 def _wg_capacity(num_seqs, group, head_dim, block_size):
     """Chunks one window of the workgroup kernel holds: 160 KiB of LDS less the
-    per-sequence arrays, over the per-chunk words (record, unit record, state)."""
+    per-sequence and per-workgroup arrays (lengths, prefix sums, per-wavefront
+    sums, four words of counters) and two spare unit records, over the
+    per-chunk words (chunk record with its table entries, unit record, unit
+    list entry, G x D accumulators and G (max, sum) pairs)."""
     up4 = lambda w: (w + 3) // 4 * 4
-    nw = 8 if head_dim <= 64 else 4
+    nw = 6 if head_dim <= 64 else 4
     nb = 1 if block_size >= 32 else 32 // block_size
-    fixed = up4(num_seqs) + up4(num_seqs + 1) + up4(nw) + 4
-    per_chunk = 5 + nb + 3 + group * head_dim + 2 * group
-    return min((160 * 1024 // 4 - fixed - 12) // per_chunk, 1024)
+    fixed = up4(up4(up4(up4(num_seqs) + num_seqs + 1) + nw) + 4)
+    per_chunk = (5 + nb) + 4 + 1 + group * head_dim + 2 * group
+    return min((160 * 1024 // 4 - fixed - 2 * 4 - 16) // per_chunk, 1024)
 
 
 def test_workspace_size_rules_stream_wg():
@@ -139,11 +142,12 @@ def test_workspace_size_rules_stream_wg():
     assert ws(d) == 256 + region(17 * 4 * 64 * 4) + region(17 * 4 * 2 * 4)
     assert zb(d) == 256
     assert ws(_dims()) == ws(d)  # AUTO with no partition size runs this kernel
-    # stream_waves rounds up to whole workgroups of 8 wavefronts: 9 -> 2 groups
+    # stream_waves (a multiple of 4) rounds up to whole workgroups of 6
+    # wavefronts at head_dim 64: 64 -> 11 groups, 68 -> 12
     d2 = _dims(kernel=4, stream_waves=64)
-    assert ws(d2) == 256 + region((16 + 8) * 4 * 64 * 4) + region((16 + 8) * 4 * 2 * 4)
+    assert ws(d2) == 256 + region((16 + 11) * 4 * 64 * 4) + region((16 + 11) * 4 * 2 * 4)
     d3 = _dims(kernel=4, stream_waves=68)
-    assert ws(d3) == 256 + region((16 + 9) * 4 * 64 * 4) + region((16 + 9) * 4 * 2 * 4)
+    assert ws(d3) == 256 + region((16 + 12) * 4 * 64 * 4) + region((16 + 12) * 4 * 2 * 4)
     # batch 64 x 8 KV heads up to 2048 tokens: 32768 chunks over 256 workgroups
     # is 128 per workgroup, within one window's capacity
     cap = _wg_capacity(64, 4, 64, 16)
