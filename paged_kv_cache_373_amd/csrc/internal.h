@@ -180,6 +180,7 @@ struct PrefillLaunch {
   float scale_log2;
   int32_t out_f32;
   void* out;                   // [num_tokens, Hq, D]
+  int32_t wg_per_pair;         // workgroups per (sequence, KV head) (set by the launcher)
 };
 bool prefill_shape_supported(int head_dim, int block_size, int group);
 

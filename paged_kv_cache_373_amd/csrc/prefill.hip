@@ -42,6 +42,101 @@ constexpr int kNW = 4;  // wavefronts per workgroup
 // registers.
 constexpr int prefill_tiles_per_wave(int head_dim) { return head_dim <= 64 ? 3 : 1; }
 
+// One chunk folded into the states of TPW tiles at once: the arithmetic of
+// Mfma<D, BS>::step for each tile, regrouped by phase - every tile's QK^T
+// products, then every tile's masks and row maxima, one uniform test for a
+// rescale in any tile (rare: the maximum moves past the margin), then every
+// tile's exponentials and P.V products.  Each phase is one straight run of
+// independent instructions over the tiles, which the compiler interleaves;
+// per tile the operations and their order are the step's, so the results are
+// the same bits.  With kCausal, lim[t] is how many of the chunk's tokens the
+// lane's row of tile t may see.
+template <int D, int BS, int TPW, bool kCausal>
+__device__ __forceinline__ void step_tiles(const bf16x8_t (&qop)[TPW][D / 32],
+                                           typename Mfma<D, BS>::Regs& x, int valid, float sl,
+                                           int c, typename Mfma<D, BS>::State (&st)[TPW],
+                                           const int (&lim)[TPW]) {
+  constexpr int HS = D / 32;
+  constexpr int NT = D / 16;
+  f32x4_t s0[TPW], s1[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    s0[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    s1[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int hs = 0; hs < HS; ++hs) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[0][hs], qop[t][hs], s0[t], 0, 0, 0);
+      s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[1][hs], qop[t][hs], s1[t], 0, 0, 0);
+    }
+  }
+  const bool tail = valid < 32;  // wave-uniform
+  const int lv = valid - 8 * c;  // tokens of this lane group still in range
+  float xs[TPW][8];
+  float cm[TPW];
+  bool need = false;
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xs[t][i] = s0[t][i];
+      xs[t][4 + i] = s1[t][i];
+    }
+    if constexpr (kCausal) {
+      const int lvc = min(valid, lim[t]) - 8 * c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[t][e] = (e < lvc) ? xs[t][e] : -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xs[t][e] = (!tail || e < lv) ? xs[t][e] : -INFINITY;
+    }
+    cm[t] = maxnan(maxnan(xs[t][0], xs[t][1], xs[t][2]), maxnan(xs[t][3], xs[t][4], xs[t][5]),
+                   maxnan(xs[t][6], xs[t][7]));
+    cm[t] = max_over_rows(cm[t]) * sl;
+    need = need || cm[t] > st[t].m2 + kRescaleThreshold;
+  }
+  if (__ballot(need) != 0) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (__ballot(cm[t] > st[t].m2 + kRescaleThreshold) != 0) {
+        const float mn = fmaxf(st[t].m2, cm[t]);
+        const float alpha = fast_exp2(st[t].m2 - mn);  // 0 on the first chunk (m2 = -inf)
+        st[t].m2 = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = __shfl(alpha, 4 * c + i);  // factor of row 4 c + i
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) st[t].acc[nt][i] *= a;
+          st[t].lsum[i] *= a;
+        }
+      }
+    }
+  }
+  bf16x8_t pa[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pa[t][e] = static_cast<__bf16>(fast_exp2(fmaf(xs[t][e], sl, -st[t].m2)));
+  if (tail) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x.v[nt][e] = (e < lv) ? x.v[nt][e] : static_cast<__bf16>(0.f);
+  }
+  const bf16x8_t ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      st[t].acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], x.v[nt], st[t].acc[nt], 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    st[t].lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[t], ones, st[t].lsum, 0, 0, 0);
+}
+
 template <int D, int BS>
 __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
     prefill_mfma(const PrefillLaunch a) {
@@ -55,8 +150,19 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
   constexpr int kBatchChunks = 64 / NB;  // chunks whose blocks one batch of lane loads covers
   constexpr int TPW = prefill_tiles_per_wave(D);
 
-  const int b = blockIdx.z;
-  const int h = blockIdx.y;
+  // XCD-aware placement: consecutive workgroups go to the eight XCDs in turn,
+  // and each XCD has an L2 of its own.  Workgroup L serves (sequence, KV head)
+  // pair p = 8 (L / 8 / W) + L % 8 and its item block (L / 8) % W, so every
+  // workgroup of a pair runs on the same XCD and the pair's K/V, which all of
+  // its items read, is fetched into that XCD's L2 only.
+  const int W = a.wg_per_pair;
+  const int L = blockIdx.x;
+  const int t8 = L >> 3;
+  const int pair = 8 * (t8 / W) + (L & 7);
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int b = pair / a.num_kv_heads;
+  const int h = pair - b * a.num_kv_heads;
+  const int wblk = t8 - (t8 / W) * W;  // this workgroup's block of items within the pair
   const int lane = threadIdx.x & 63;
   const int c = lane >> 4;
   const int r = lane & 15;
@@ -73,8 +179,8 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
   const int nq = q1 - q0;
   const int T = a.seq_lens[b];
   const int ntiles = (nq * G + 15) / 16;
-  const int wave0 = blockIdx.x * kNW + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * kNW;
+  const int wave0 = wblk * kNW + (threadIdx.x >> 6);
+  const int nwaves = W * kNW;
   if (nq > T || T > a.max_blocks_per_seq * BS) {
     for (int e = wave0 * 64 + lane; e < nq * G * D; e += nwaves * 64) {
       const int row = e / (G * D);
@@ -145,13 +251,13 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
         const int t0 = 32 * (k0 + kb);
         if (pos_min - t0 >= 31) {
           // every row of the item sees the whole chunk: no mask to apply
-#pragma unroll
-          for (int t = 0; t < TPW; ++t) M::step(qop[t], sl8.x, 32, sl, c, st[t]);
+          step_tiles<D, BS, TPW, false>(qop, sl8.x, 32, sl, c, st, pos);
         } else {
           const int valid = min(32, T - t0);
+          int lim[TPW];
 #pragma unroll
-          for (int t = 0; t < TPW; ++t)
-            M::template step<true>(qop[t], sl8.x, valid, sl, c, st[t], pos[t] - t0 + 1);
+          for (int t = 0; t < TPW; ++t) lim[t] = pos[t] - t0 + 1;
+          step_tiles<D, BS, TPW, true>(qop, sl8.x, valid, sl, c, st, lim);
         }
       };
       // every refill issues its loads (one past the batch re-reads its last
@@ -225,8 +331,16 @@ hipError_t launch_prefill(const PrefillLaunch& a, int max_q_len, hipStream_t str
   const int tiles = (max_q_len * a.group + 15) / 16;
   const int tpw = prefill_tiles_per_wave(a.head_dim);
   const int items = (tiles + tpw - 1) / tpw;
-  const dim3 grid(static_cast<unsigned>((items + kNW - 1) / kNW), a.num_kv_heads, a.num_seqs);
-  return a.head_dim == 64 ? launch_d<64>(a, grid, stream) : launch_d<128>(a, grid, stream);
+  PrefillLaunch la = a;
+  la.wg_per_pair = (items + kNW - 1) / kNW;
+  if (la.wg_per_pair < 1) la.wg_per_pair = 1;
+  // eight workgroups (one per XCD) per group of eight (sequence, KV head)
+  // pairs and item block; the ones past the last pair exit at once
+  const int64_t pair_groups = (static_cast<int64_t>(a.num_seqs) * a.num_kv_heads + 7) / 8;
+  const int64_t wgs = 8 * pair_groups * la.wg_per_pair;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(wgs));
+  return a.head_dim == 64 ? launch_d<64>(la, grid, stream) : launch_d<128>(la, grid, stream);
 }
 
 }  // namespace pkv
