@@ -379,14 +379,17 @@ def run_prefix_cow(args) -> int:
                                                  max_seq_len=kw["max_seq_len"]),
                       dtype=torch.uint8, device=dev)
 
-    def casc(i):
-        kc, vc = caches[i % copies]
-        pkv.cascade_decode(q, kc, vc, bt, lens, gs, pl, bs, w.scale, out,
-                           max_prefix_len=int(pl_np.max()), max_seq_len=kw["max_seq_len"],
-                           workspace=cws)
+    def casc_with(kernel):
+        def casc(i):
+            kc, vc = caches[i % copies]
+            pkv.cascade_decode(q, kc, vc, bt, lens, gs, pl, bs, w.scale, out,
+                               max_prefix_len=int(pl_np.max()), max_seq_len=kw["max_seq_len"],
+                               workspace=cws, kernel=kernel)
+        return casc
 
     ms = timed(stream, dec, args.steps, args.warmup)
-    ms_casc = timed(stream, casc, args.steps, args.warmup)
+    ms_casc = timed(stream, casc_with("auto"), args.steps, args.warmup)
+    ms_casc2 = timed(stream, casc_with("mfma"), args.steps, args.warmup)
     ms_cow = timed(stream, cow, args.steps, args.warmup)
     ms_cow_gpu = timed_graph(cow, 50)
     logical = w.kv_bytes()
@@ -399,13 +402,17 @@ def run_prefix_cow(args) -> int:
         "logical_kv_bytes": logical, "logical_gbs": round(logical / (ms * 1e-3) / 1e9, 1),
         "unique_kv_bytes": unique, "unique_gbs": round(unique / (ms * 1e-3) / 1e9, 1),
         "cascade_us": round(ms_casc * 1e3, 3),
+        "cascade_kernel": pkv.cascade_plan_kernel(q, caches[0][0], bt, len(pl_np),
+                                                  int(pl_np.max()),
+                                                  max_seq_len=kw["max_seq_len"]),
+        "cascade_two_launch_us": round(ms_casc2 * 1e3, 3),
         "cascade_logical_gbs": round(logical / (ms_casc * 1e-3) / 1e9, 1),
         "cascade_unique_gbs": round(unique / (ms_casc * 1e-3) / 1e9, 1),
         "cascade_groups": int(len(pl_np)), "cascade_prefix_tokens": int(pl_np.max()),
         "cascade_roofline": {"bound": "hbm", "achieved": round(unique / (ms_casc * 1e-3) / 1e9, 1),
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(unique / (ms_casc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                             "note": "unique K/V bytes (each block once) per call of both launches"},
+                             "note": "unique K/V bytes (each block once) per call"},
         "copy_blocks_pairs": len(pairs), "copy_blocks_bytes": 2 * len(pairs) * hkv * bs * d * 2,
         "copy_blocks_us": round(ms_cow_gpu * 1e3, 3),
         "copy_blocks_us_note": "GPU time per call, 50 calls replayed from a HIP graph; "

@@ -156,6 +156,11 @@ typedef struct {
  * workspaces. */
 size_t pkv_decode_workspace_size(const pkv_decode_dims* dims, int32_t block_size);
 
+/* The form pkv_cascade_decode runs for these arguments: PKV_KERNEL_STREAM_WG
+ * (one launch) or PKV_KERNEL_MFMA (two launches); -1 when they are invalid
+ * or unsupported. */
+int32_t pkv_cascade_plan_kernel(const pkv_decode_dims* dims, int32_t num_groups,
+                                int32_t max_prefix_len, int32_t block_size);
 /* Leading bytes of the workspace that must be zero when
  * pkv_paged_attention_decode starts (and are zero again when it completes);
  * (size_t)-1 when the arguments are invalid. */
@@ -353,19 +358,26 @@ pkv_status pkv_merge_attention_states(const float* part_out, const float* part_l
  *                 same physical blocks (the first member's row is read).
  *   num_groups    1 <= num_groups <= S (when S > 0).
  *   max_prefix_len  host bound on every L_g, <= dims->max_seq_len.
- *   dims          as for pkv_paged_attention_decode; `kernel`,
- *                 `partition_size`, `waves_per_group`, `balance_partitions` and
- *                 `stream_waves` are ignored.  head_dim 64 or 128, block_size
- *                 8, 16 or 32, group <= 16, S <= 4096 (PKV_ERR_UNSUPPORTED
- *                 otherwise).
+ *   dims          as for pkv_paged_attention_decode; `partition_size`,
+ *                 `waves_per_group`, `balance_partitions` and `stream_waves`
+ *                 are ignored.  head_dim 64 or 128, block_size 8, 16 or 32,
+ *                 group <= 16, S <= 4096 (PKV_ERR_UNSUPPORTED otherwise).
+ *                 `kernel` picks the form: PKV_KERNEL_STREAM_WG one launch, a
+ *                 workgroup per (group, KV head, block of members) folding the
+ *                 group's prefix and those members' suffixes and merging in
+ *                 LDS (PKV_ERR_UNSUPPORTED when a task's chunks - the longest
+ *                 prefix plus its members' longest suffixes, from the host
+ *                 bounds - exceed its LDS records); PKV_KERNEL_MFMA two
+ *                 launches, segments' partial states then their merge; any
+ *                 other value the first when it fits, else the second.
  *   workspace     device scratch of at least pkv_cascade_workspace_size bytes,
  *                 256-byte aligned; needs no initialisation and holds garbage
  *                 after the call.
  * If a device-side condition above fails (groups not a partition of the
  * sequences, L_g not a multiple of block_size or above max_prefix_len, a
  * member shorter than L_g, some T_b above dims->max_seq_len), every output row
- * is NaN.  Two launches on `stream`: the segments' partial states, then their
- * merge.  q, k_cache and v_cache 16-byte aligned.
+ * is NaN.  q, k_cache and v_cache 16-byte aligned.  Results do not depend on
+ * timing (each form merges in a fixed order).
  * Returns PKV_OK, or an error status with nothing enqueued. */
 size_t pkv_cascade_workspace_size(const pkv_decode_dims* dims, int32_t num_groups,
                                   int32_t max_prefix_len, int32_t block_size);

@@ -23,7 +23,8 @@ from .scheduler import Batcher, Request
 __all__ = [
     "lib", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_noalloc", "reshape_and_cache",
-    "copy_blocks", "cascade_decode", "cascade_workspace_size", "paged_prefill", "swap_out",
+    "copy_blocks", "cascade_decode", "cascade_workspace_size", "cascade_plan_kernel",
+    "paged_prefill", "swap_out",
     "swap_in", "swap_buffer",
     "merge_attention_states", "decode_workspace_size", "DecodeWorkspace", "new_kv_cache",
     "BlockManager", "Batcher", "Request", "block_key",
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.pkv_merge_attention_states.restype = ctypes.c_int
         L.pkv_cascade_workspace_size.argtypes = [dims_p, i32, i32, i32]
         L.pkv_cascade_workspace_size.restype = sz
+        L.pkv_cascade_plan_kernel.argtypes = [dims_p, i32, i32, i32]
+        L.pkv_cascade_plan_kernel.restype = i32
         L.pkv_cascade_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                          ctypes.c_float, vp, dims_p, vp, sz, vp]
         L.pkv_cascade_decode.restype = ctypes.c_int
@@ -443,6 +446,18 @@ def cascade_workspace_size(q, k_cache, block_tables, num_groups: int, max_prefix
     return int(n)
 
 
+def cascade_plan_kernel(q, k_cache, block_tables, num_groups: int, max_prefix_len: int, *,
+                        max_seq_len=None, out_dtype=torch.bfloat16, kernel: str = "auto") -> str:
+    """The form :func:`cascade_decode` runs: "stream_wg" (one launch) or
+    "mfma" (two launches)."""
+    dims = _dims(q, k_cache, block_tables, max_seq_len, 0, out_dtype, kernel, 0, False)
+    k = lib().pkv_cascade_plan_kernel(ctypes.byref(dims), int(num_groups), int(max_prefix_len),
+                                      k_cache.shape[2])
+    if k not in (_KERNELS["stream_wg"], _KERNELS["mfma"]):
+        raise PagedKVError(PKV_ERR_INVALID, "pkv_cascade_plan_kernel")
+    return "stream_wg" if k == _KERNELS["stream_wg"] else "mfma"
+
+
 _cascade_ws = {}
 
 
@@ -451,7 +466,7 @@ def cascade_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    group_starts: torch.Tensor, prefix_lens: torch.Tensor, block_size: int,
                    scale: float, out: torch.Tensor, *, max_prefix_len: int,
                    max_seq_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                   stream=None) -> torch.Tensor:
+                   kernel: str = "auto", stream=None) -> torch.Tensor:
     """Shared-prefix decode ([PU §共享前缀，分叉时 Copy-on-write]; [PU §按 Block
     分配]): the same result as :func:`paged_attention_decode`, with the blocks
     a group of sequences shares read once per group.  Group g is the
@@ -459,7 +474,10 @@ def cascade_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     device), sharing their first ``prefix_lens[g]`` tokens (int32 [NG], whole
     blocks); :meth:`BlockManager.shared_prefix_groups` derives both from the
     tables.  ``workspace`` is a uint8 device tensor (default: one per device,
-    grown as needed); it needs no initialisation."""
+    grown as needed); it needs no initialisation.  ``kernel``: "stream_wg"
+    (one launch, a workgroup per group, KV head and block of members),
+    "mfma" (two launches: segments, then their merge) or "auto" (the first
+    when a task fits its LDS records)."""
     _check(q, "q", torch.bfloat16, 3)
     _check(k_cache, "k_cache", torch.bfloat16, 4)
     _check(v_cache, "v_cache", torch.bfloat16, 4)
@@ -479,7 +497,9 @@ def cascade_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     ng = prefix_lens.shape[0]
     if group_starts.shape[0] != ng + 1:
         raise ValueError("group_starts must hold num_groups + 1 entries")
-    dims = _dims(q, k_cache, block_tables, max_seq_len, 0, out.dtype, "auto", 0, False)
+    if kernel not in ("auto", "stream_wg", "mfma"):
+        raise ValueError("cascade kernel must be 'auto', 'stream_wg' or 'mfma'")
+    dims = _dims(q, k_cache, block_tables, max_seq_len, 0, out.dtype, kernel, 0, False)
     L = lib()
     need = L.pkv_cascade_workspace_size(ctypes.byref(dims), ng, int(max_prefix_len), bs)
     if need == ctypes.c_size_t(-1).value:

@@ -444,6 +444,7 @@ struct CascadePlan {
   int32_t group;
   int64_t max_pre_items, max_suf_items;
   int32_t waves;
+  int32_t use_wg, members_per_task, wg_grid, wg_chunks;  // the one-launch workgroup form
   // workspace: [pre_acc | pre_ml | suf_acc | suf_ml | tables]
   size_t pre_ml_offset, suf_acc_offset, suf_ml_offset, tables_offset, workspace_bytes;
 };
@@ -464,6 +465,7 @@ CascadePlan plan_cascade(const pkv_decode_dims* d, int32_t num_groups, int32_t m
   if (num_groups < 0 || (d->num_seqs > 0 && (num_groups < 1 || num_groups > d->num_seqs)))
     return p;
   if (max_prefix_len < 0 || max_prefix_len > d->max_seq_len) return p;
+  if (d->kernel < PKV_KERNEL_AUTO || d->kernel > PKV_KERNEL_STREAM_WG) return p;
   p.group = d->num_q_heads / d->num_kv_heads;
   if (!pkv::cascade_shape_supported(d->head_dim, block_size, p.group, d->num_seqs))
     return (p.status = PKV_ERR_UNSUPPORTED, p);
@@ -494,6 +496,31 @@ CascadePlan plan_cascade(const pkv_decode_dims* d, int32_t num_groups, int32_t m
   p.suf_ml_offset = p.suf_acc_offset + suf_acc;
   p.tables_offset = p.suf_ml_offset + suf_ml;
   p.workspace_bytes = p.tables_offset + tables;
+  // The one-launch workgroup form: a task is (group, KV head, block of
+  // members); members per task as many as one 16-row tile holds, halved
+  // while the tasks would not give every compute unit a workgroup.  It runs
+  // when a task's chunks (the longest prefix plus its members' longest
+  // suffixes) fit the records in LDS.
+  {
+    const int64_t kUnits = 256;  // compute units of an MI355X
+    int64_t mpt = pkv::kCascadeRows / G;
+    while (mpt > 1 && Hkv * div_up(S, mpt) < kUnits) mpt /= 2;
+    const int64_t bound = div_up(max_prefix_len, 32) + mpt * div_up(d->max_seq_len, 32);
+    const pkv::CascadeWgLayout lay = pkv::cascade_wg_layout(
+        d->head_dim, block_size, static_cast<int>(S), static_cast<int>(NG), 0);
+    const bool fits = bound >= 1 && bound <= lay.capacity;
+    p.wg_chunks = static_cast<int32_t>(fits ? bound : 0);
+    if (d->kernel == PKV_KERNEL_STREAM_WG && !fits) return (p.status = PKV_ERR_UNSUPPORTED, p);
+    p.use_wg = (d->kernel != PKV_KERNEL_MFMA && fits) ? 1 : 0;
+    p.members_per_task = static_cast<int32_t>(mpt);
+    // at least the tasks of any grouping, one workgroup per compute unit at
+    // most (each asks for the whole LDS, so the dispatcher spreads them over
+    // all units; stacking two on a unit while others idle measured slower)
+    const int64_t tasks = Hkv * (NG + div_up(S, mpt));
+    int64_t grid = tasks < kUnits ? tasks : kUnits;
+    grid = (grid + 7) / 8 * 8;
+    p.wg_grid = static_cast<int32_t>(grid < 8 ? 8 : grid);
+  }
   p.ok = true;
   p.status = PKV_OK;
   return p;
@@ -502,6 +529,13 @@ CascadePlan plan_cascade(const pkv_decode_dims* d, int32_t num_groups, int32_t m
 }  // namespace
 
 extern "C" {
+
+int32_t pkv_cascade_plan_kernel(const pkv_decode_dims* dims, int32_t num_groups,
+                                int32_t max_prefix_len, int32_t block_size) {
+  const CascadePlan p = plan_cascade(dims, num_groups, max_prefix_len, block_size);
+  if (!p.ok) return -1;
+  return p.use_wg ? PKV_KERNEL_STREAM_WG : PKV_KERNEL_MFMA;
+}
 
 size_t pkv_cascade_workspace_size(const pkv_decode_dims* dims, int32_t num_groups,
                                   int32_t max_prefix_len, int32_t block_size) {
@@ -556,6 +590,10 @@ pkv_status pkv_cascade_decode(const void* q, const void* k_cache, const void* v_
   a.max_pre_items = p.max_pre_items;
   a.max_suf_items = p.max_suf_items;
   a.waves = p.waves;
+  a.use_wg = p.use_wg;
+  a.members_per_task = p.members_per_task;
+  a.wg_grid = p.wg_grid;
+  a.wg_chunks = p.wg_chunks;
   return hip_status(pkv::launch_cascade(a, static_cast<hipStream_t>(stream)));
 }
 

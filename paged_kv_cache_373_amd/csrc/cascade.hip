@@ -52,14 +52,14 @@ __host__ __device__ constexpr int cascade_lds_ints(int S, int NG) {
   return (NG + 1) + (S + 1) + S + S + (NG + 1) + NG + kNW + 1;
 }
 
-// Exclusive prefix of count(0 .. n-1) into pre[0 .. n], by all kNTH threads
+// Exclusive prefix of count(0 .. n-1) into pre[0 .. n], by all NTH threads
 // (count(i) is evaluated twice by the thread owning i and must not change in
-// between); s_wsum holds kNW ints.  Ends with a barrier.
-template <typename F>
+// between); s_wsum holds NTH / 64 ints.  Ends with a barrier.
+template <int NTH = kNTH, typename F>
 __device__ void block_scan(int n, F count, int* pre, int* s_wsum, int tid) {
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int per = (n + kNTH - 1) / kNTH;  // thread tid owns [tid per, tid per + per)
+  const int per = (n + NTH - 1) / NTH;  // thread tid owns [tid per, tid per + per)
   int mine = 0;
   for (int j = 0; j < per; ++j) {
     const int i = tid * per + j;
@@ -82,7 +82,7 @@ __device__ void block_scan(int n, F count, int* pre, int* s_wsum, int tid) {
       run += count(i);
     }
   }
-  if (tid == kNTH - 1) pre[n] = run;
+  if (tid == NTH - 1) pre[n] = run;
   __syncthreads();
 }
 
@@ -440,6 +440,365 @@ hipError_t launch_bs(const CascadeLaunch& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// One-launch form.  A task is (group g, KV head h, member block): up to
+// members_per_task consecutive members of g, whose query rows R = m G + gh
+// (m the member within the block) fill at most one 16-row matrix-core tile.
+// The task's chunks are the group's prefix chunks (every row of the task
+// attends them) followed by each member's suffix chunks (only that member's
+// rows attend them; the other rows' scores are masked to -inf), 32 tokens
+// each.  One workgroup runs a task: wavefront w folds chunks w, w + NW, ...
+// into one running state of the tile's rows, then the NW states are merged in
+// LDS in wavefront order and each row is written out.  Nothing crosses
+// workgroups, so there is no device-scope hand-off; the static split of the
+// chunks and the fixed merge order make the result bit-reproducible.  The
+// tasks of one (g, h) are neighbours in task order and run on one XCD, so the
+// group's prefix blocks come from that XCD's L2 after the first read.
+//
+// A row's running maximum starts at kEmptyMax (finite) rather than -inf, so a
+// row that has attended nothing yet stays at exp2(-inf) = 0 for masked scores
+// and at a rescale factor of 1, without a select in the fold.
+constexpr float kEmptyMax = -1.0e30f;
+// Wavefronts of a task's workgroup: one per SIMD (on prefix_cow, 15.2 us
+// against 16.4 us with two per SIMD: each wavefront then folds twice the
+// chunks, and fewer states are merged at the end).
+constexpr int cascade_wg_waves(int head_dim) { return head_dim <= 64 ? 4 : 4; }
+
+template <int D, int BS, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
+    cascade_wg(const CascadeLaunch a, const CascadeWgLayout lay) {
+  using M = Mfma<D, BS>;
+  using Regs = typename M::Regs;
+  constexpr int NB = M::NB;
+  constexpr int HS = M::HS;
+  constexpr int NT = M::NT;
+  constexpr int NTH = NW * 64;
+  constexpr int E4 = D / 4;
+  constexpr int kRec = 2 + NB;  // member (-1: prefix), valid tokens, physical blocks
+
+  const int S = a.num_seqs;
+  const int NG = a.num_groups;
+  const int Hkv = a.num_kv_heads;
+  const int Hq = a.num_q_heads;
+  const int G = a.group;
+  const int MB = a.max_blocks_per_seq;
+  const int mpt = a.members_per_task;
+  extern __shared__ __align__(16) int lds[];
+  int* s_len = lds + lay.off_len;    // [S] seq_lens
+  int* s_gs = lds + lay.off_gs;      // [NG + 1] group_starts
+  int* s_pl = lds + lay.off_pl;      // [NG] prefix_lens
+  int* s_gof = lds + lay.off_gof;    // [S] group of sequence b
+  int* s_tpre = lds + lay.off_tpre;  // [NG + 1] tasks before group g's
+  int* s_misc = lds + lay.off_misc;  // [NW] scan partials, [NW] error flag
+  int* s_mpre = lds + lay.off_mpre;  // [kCascadeRows + 1] suffix chunks before member m's
+  int* s_rec = lds + lay.off_rec;    // [capacity][kRec] the task's chunk records
+  float* s_acc = reinterpret_cast<float*>(lds + lay.off_acc);  // [NW][16][D]
+  float* s_ml = reinterpret_cast<float*>(lds + lay.off_ml);    // [NW][16][max, sum]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane >> 4;
+  const int r = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // 1. The lengths and groups, and the checks of what lives in device memory
+  // (as for the item form: the groups partition [0, S) into non-empty runs,
+  // prefixes are whole blocks within the host's bound, no member is shorter
+  // than its group's prefix or longer than the host's bound).  Every
+  // workgroup reaches the same verdict; a violation makes every row NaN.
+  for (int i = tid; i < S; i += NTH) s_len[i] = a.seq_lens[i];
+  for (int i = tid; i <= NG; i += NTH) s_gs[i] = a.group_starts[i];
+  for (int i = tid; i < NG; i += NTH) s_pl[i] = a.prefix_lens[i];
+  if (tid == 0) s_misc[NW] = 0;
+  __syncthreads();
+  for (int g = tid; g < NG; g += NTH) {
+    const int b0 = s_gs[g];
+    const int b1 = s_gs[g + 1];
+    const int L = s_pl[g];
+    const bool bad = b0 < 0 || b1 <= b0 || b1 > S || (g == 0 && b0 != 0) ||
+                     (g == NG - 1 && b1 != S) || L < 0 || L % BS != 0 ||
+                     L > a.max_prefix_len;
+    if (bad) {
+      s_misc[NW] = 1;
+    } else {
+      for (int b = b0; b < b1; ++b) s_gof[b] = g;
+    }
+  }
+  __syncthreads();
+  if (s_misc[NW] == 0) {
+    for (int b = tid; b < S; b += NTH) {
+      const int T = s_len[b];
+      if (T < s_pl[s_gof[b]] || T > a.max_seq_len) s_misc[NW] = 1;
+    }
+    block_scan<NTH>(
+        NG, [&](int g) { return Hkv * div_up(s_gs[g + 1] - s_gs[g], mpt); }, s_tpre, s_misc,
+        tid);
+  }
+  __syncthreads();
+  if (s_misc[NW] != 0) {
+    for (int b = blockIdx.x; b < S; b += gridDim.x)
+      for (int e = tid; e < Hq * D; e += NTH)
+        store_out(a.out, static_cast<size_t>(b) * Hq * D + e, NAN, a.out_f32);
+    return;
+  }
+
+  const float sl = a.scale_log2;
+  const size_t blk_stride = static_cast<size_t>(Hkv) * M::kTile;
+  const typename M::Lane ln(c, r);
+  struct Slot {
+    Regs x;
+    int pos;
+  };
+  const int ntask = s_tpre[NG];
+  // XCD-aware order: workgroup L starts at task (L % 8) (grid / 8) + L / 8,
+  // so consecutive tasks run on one XCD (workgroups go to the XCDs in turn)
+  const int grid = gridDim.x;
+  const int L8 = blockIdx.x;
+  const int tau0 = (grid % 8 == 0) ? (L8 & 7) * (grid >> 3) + (L8 >> 3) : L8;
+  for (int tau = tau0; tau < ntask; tau += grid) {
+    // 2. The task: its group, head and member block.
+    int lo = 0, hi = NG;  // the group: largest g with s_tpre[g] <= tau
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tpre[mid] <= tau) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int b0 = s_gs[g];
+    const int F = s_gs[g + 1] - b0;
+    const int L = s_pl[g];
+    const int nblk = div_up(F, mpt);
+    const int rem = tau - s_tpre[g];
+    const int h = rem / nblk;
+    const int m0 = (rem - h * nblk) * mpt;
+    const int mc = min(mpt, F - m0);  // members of this task
+    const int nP = div_up(L, 32);     // prefix chunks
+    if (tid == 0) {
+      int run = 0;
+      for (int m = 0; m < mc; ++m) {
+        s_mpre[m] = run;
+        run += div_up(s_len[b0 + m0 + m] - L, 32);
+      }
+      s_mpre[mc] = run;
+    }
+    __syncthreads();
+    const int n = nP + s_mpre[mc];  // the task's chunks
+    if (n > lay.capacity) {
+      // (cannot happen for lengths within the host's bounds, which size the
+      // launch; a task past them gets NaN rows rather than records past LDS)
+      for (int e = tid; e < mc * G * D; e += NTH) {
+        const int R = e / D;
+        const int m = R / G;
+        store_out(a.out, (static_cast<size_t>(b0 + m0 + m) * Hq + h * G + (R - m * G)) * D +
+                             (e - R * D), NAN, a.out_f32);
+      }
+      __syncthreads();
+      continue;
+    }
+
+    // 3. The chunk records: member (-1: prefix), valid tokens, physical blocks.
+    for (int i = tid; i < n; i += NTH) {
+      int member, tok0, last_blk;
+      const int32_t* row;
+      if (i < nP) {
+        member = -1;
+        tok0 = 32 * i;
+        row = a.block_tables + static_cast<size_t>(b0) * MB;  // every member's row holds the prefix
+        last_blk = (L - 1) / BS;
+        s_rec[i * kRec + 1] = min(32, L - tok0);
+      } else {
+        const int j = i - nP;
+        int m = 0;
+        while (m + 1 < mc && s_mpre[m + 1] <= j) ++m;
+        const int T = s_len[b0 + m0 + m];
+        member = m;
+        tok0 = L + 32 * (j - s_mpre[m]);
+        row = a.block_tables + static_cast<size_t>(b0 + m0 + m) * MB;
+        last_blk = (T - 1) / BS;
+        s_rec[i * kRec + 1] = min(32, T - tok0);
+      }
+      s_rec[i * kRec] = member;
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb)
+        s_rec[i * kRec + 2 + jb] = row[min(min(tok0 / BS + jb, last_blk), MB - 1)];
+    }
+    __syncthreads();
+
+    // 4. The tile's query rows as the QK^T B operand: lane (c, r) holds dims
+    // [32 hs + 8 c, +8) of row r (member r / G, head r % G).  Rows past the
+    // task's members read member 0's row; they attend nothing (always masked)
+    // and are not written.
+    const int rm = r / G;
+    const bool live = r < mc * G;
+    const uint16_t* qrow =
+        a.q + (static_cast<size_t>(b0 + m0 + (live ? rm : 0)) * Hq + h * G + (live ? r - rm * G : 0)) *
+                  D + 8 * c;
+    bf16x8_t qop[HS];
+    const size_t head_off = static_cast<size_t>(h) * M::kTile;
+    auto issue = [&](int pos, Slot& sl8) __attribute__((always_inline)) {
+      const int* rec = s_rec + pos * kRec;
+      size_t base[NB];
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb)
+        base[jb] = static_cast<size_t>(__builtin_amdgcn_readfirstlane(rec[2 + jb])) * blk_stride +
+                   head_off;
+      M::load(a.k_cache, a.v_cache, base, ln, sl8.x);
+      sl8.pos = pos;
+    };
+    typename M::State st;
+    st.reset();
+    st.m2 = kEmptyMax;
+    // One chunk into the state: Mfma::step with the rows the chunk does not
+    // belong to masked out.
+    auto consume = [&](Slot& sl8) __attribute__((always_inline)) {
+      const int* rec = s_rec + sl8.pos * kRec;
+      const int member = __builtin_amdgcn_readfirstlane(rec[0]);
+      const int valid = __builtin_amdgcn_readfirstlane(rec[1]);
+      const bool active = live && (member < 0 || member == rm);
+      f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl8.x.k[0][hs], qop[hs], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sl8.x.k[1][hs], qop[hs], s1, 0, 0, 0);
+      }
+      const int lv = active ? valid - 8 * c : 0;  // this lane's tokens its row attends
+      float xs[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xs[i] = (i < lv) ? s0[i] : -INFINITY;
+        xs[4 + i] = (4 + i < lv) ? s1[i] : -INFINITY;
+      }
+      float cm = maxnan(maxnan(xs[0], xs[1], xs[2]), maxnan(xs[3], xs[4], xs[5]),
+                        maxnan(xs[6], xs[7]));
+      cm = max_over_rows(cm) * sl;
+      if (__ballot(cm > st.m2 + kRescaleThreshold) != 0) {
+        const float mn = fmaxf(st.m2, cm);
+        const float alpha = fast_exp2(st.m2 - mn);
+        st.m2 = mn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float f = __shfl(alpha, 4 * c + i);  // factor of row 4 c + i
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) st.acc[nt][i] *= f;
+          st.lsum[i] *= f;
+        }
+      }
+      bf16x8_t pa;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(fast_exp2(fmaf(xs[e], sl, -st.m2)));
+      if (valid < 32) {
+        const int vv = valid - 8 * c;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            sl8.x.v[nt][e] = (e < vv) ? sl8.x.v[nt][e] : static_cast<__bf16>(0.f);
+      }
+      const bf16x8_t ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, sl8.x.v[nt], st.acc[nt], 0, 0, 0);
+      st.lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, ones, st.lsum, 0, 0, 0);
+    };
+
+    // 5. Wavefront w folds chunks w, w + NW, ... through a ring of two (a
+    // refill past its last chunk re-reads its first, which is not folded
+    // again, so every refill issues its loads and the wait counts stay exact).
+    const int nmine = n > w ? (n - w + NW - 1) / NW : 0;
+    if (nmine > 0) {
+      // (the query rows load between the ring's two first chunks: the first
+      // fold then waits for the first chunk and the rows, not the second)
+      Slot ring[2];
+      issue(w, ring[0]);
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) qop[hs] = load_bf16x8(qrow + 32 * hs);
+      issue(nmine > 1 ? w + NW : w, ring[1]);
+      for (int k = 0;;) {
+        if (k >= nmine) break;
+        consume(ring[0]);
+        issue(k + 2 < nmine ? w + (k + 2) * NW : w, ring[0]);
+        ++k;
+        if (k >= nmine) break;
+        consume(ring[1]);
+        issue(k + 2 < nmine ? w + (k + 2) * NW : w, ring[1]);
+        ++k;
+      }
+    }
+
+    // 6. The wavefronts' states into LDS (lane (c, r) holds row 4 c + i's
+    // accumulator for features 16 nt + r and its sum, and row r's maximum),
+    // then merged in wavefront order and written out.
+    {
+      float* sa = s_acc + static_cast<size_t>(w) * kCascadeRows * D;
+      float* sm = s_ml + w * kCascadeRows * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * c + i;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sa[row * D + 16 * nt + r] = st.acc[nt][i];
+        if (r == 0) sm[row * 2 + 1] = st.lsum[i];
+      }
+      if (c == 0) sm[r * 2] = st.m2;
+    }
+    __syncthreads();
+    for (int e = tid; e < mc * G * E4; e += NTH) {
+      const int R = e / E4;
+      const int d4 = e - R * E4;
+      // every state's values read first (independent LDS reads), then folded
+      // in wavefront order; a wavefront that attended none of the row's tokens
+      // (sum 0, maximum kEmptyMax) adds nothing
+      float pm[NW], pl[NW];
+      f32x4_t pa[NW];
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) {
+        pm[wv] = s_ml[(wv * kCascadeRows + R) * 2];
+        pl[wv] = s_ml[(wv * kCascadeRows + R) * 2 + 1];
+        pa[wv] = *reinterpret_cast<const f32x4_t*>(
+            s_acc + (static_cast<size_t>(wv) * kCascadeRows + R) * D + 4 * d4);
+      }
+      float mx = kEmptyMax;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) mx = fmaxf(mx, pm[wv]);
+      float den = 0.f;
+      f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) {
+        const float fj = fast_exp2(pm[wv] - mx);
+        den += pl[wv] * fj;
+        num += pa[wv] * fj;
+      }
+      // a member with no tokens (T = 0) has an all-zero row
+      const f32x4_t o = den > 0.f ? num * (1.0f / den) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int m = R / G;
+      const size_t orow =
+          (static_cast<size_t>(b0 + m0 + m) * Hq + h * G + (R - m * G)) * D + 4 * d4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) store_out(a.out, orow + t, o[t], a.out_f32);
+    }
+    __syncthreads();  // the task's records, states and member prefix are done with
+  }
+}
+
+template <int D, int BS, int NW>
+hipError_t launch_wg_bs(const CascadeLaunch& a, const CascadeWgLayout& lay, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&cascade_wg<D, BS, NW>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kCascadeLdsBytes);
+  if (attr != hipSuccess) return attr;
+  cascade_wg<D, BS, NW><<<dim3(a.wg_grid), dim3(NW * 64), static_cast<size_t>(lay.words) * 4,
+                          stream>>>(a, lay);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_wg_d(const CascadeLaunch& a, const CascadeWgLayout& lay, hipStream_t stream) {
+  constexpr int NW = cascade_wg_waves(D);
+  switch (a.block_size) {
+    case 8: return launch_wg_bs<D, 8, NW>(a, lay, stream);
+    case 16: return launch_wg_bs<D, 16, NW>(a, lay, stream);
+    default: return launch_wg_bs<D, 32, NW>(a, lay, stream);
+  }
+}
+
 template <int D>
 hipError_t launch_d(const CascadeLaunch& a, hipStream_t stream) {
   switch (a.block_size) {
@@ -457,7 +816,51 @@ bool cascade_shape_supported(int head_dim, int block_size, int group, int num_se
          group <= 16 && num_seqs <= kCascadeMaxSeqs;
 }
 
+CascadeWgLayout cascade_wg_layout(int head_dim, int block_size, int num_seqs, int num_groups,
+                                  int64_t want_chunks) {
+  CascadeWgLayout lay = {};
+  const int nw = cascade_wg_waves(head_dim);
+  const int nb = block_size >= 32 ? 1 : 32 / block_size;
+  auto up4 = [](int64_t x) { return static_cast<int32_t>((x + 3) / 4 * 4); };
+  int32_t w = 0;
+  lay.off_len = w;
+  w = up4(w + num_seqs);
+  lay.off_gs = w;
+  w = up4(w + num_groups + 1);
+  lay.off_pl = w;
+  w = up4(w + num_groups);
+  lay.off_gof = w;
+  w = up4(w + num_seqs);
+  lay.off_tpre = w;
+  w = up4(w + num_groups + 1);
+  lay.off_misc = w;
+  w = up4(w + 2 * nw);
+  lay.off_mpre = w;
+  w = up4(w + kCascadeRows + 1);
+  lay.off_acc = w;
+  w = up4(w + static_cast<int64_t>(nw) * kCascadeRows * head_dim);
+  lay.off_ml = w;
+  w = up4(w + nw * kCascadeRows * 2);
+  lay.off_rec = w;
+  const int64_t left = kCascadeLdsBytes / 4 - w;
+  const int rec = 2 + nb;
+  int64_t cap = left > 0 ? left / rec : 0;
+  if (want_chunks > 0 && want_chunks < cap) cap = want_chunks;
+  lay.capacity = static_cast<int32_t>(cap);
+  lay.words = lay.capacity > 0 ? up4(w + static_cast<int64_t>(lay.capacity) * rec) : w;
+  return lay;
+}
+
 hipError_t launch_cascade(const CascadeLaunch& a, hipStream_t stream) {
+  if (a.use_wg) {
+    if (a.wg_grid < 1 || a.members_per_task < 1 || a.members_per_task * a.group > kCascadeRows)
+      return hipErrorInvalidValue;
+    // all of the LDS: one workgroup per compute unit
+    const CascadeWgLayout lay =
+        cascade_wg_layout(a.head_dim, a.block_size, a.num_seqs, a.num_groups, 0);
+    if (lay.capacity < a.wg_chunks) return hipErrorInvalidValue;
+    return a.head_dim == 64 ? launch_wg_d<64>(a, lay, stream) : launch_wg_d<128>(a, lay, stream);
+  }
   if (a.waves < kNW || a.waves % kNW != 0) return hipErrorInvalidValue;
   return a.head_dim == 64 ? launch_d<64>(a, stream) : launch_d<128>(a, stream);
 }

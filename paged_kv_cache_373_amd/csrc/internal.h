@@ -161,8 +161,21 @@ struct CascadeLaunch {
   int32_t max_prefix_len, max_seq_len;  // host bounds the device lengths are checked against
   int64_t max_pre_items, max_suf_items;
   int32_t waves;    // launch 1 wavefronts (a multiple of 4)
+  // the one-launch workgroup form (used when use_wg): members per task and
+  // the workgroups launched
+  int32_t use_wg, members_per_task, wg_grid, wg_chunks;  // wg_chunks: records a task may need
+};
+// LDS of the workgroup form, in 4-byte words; capacity = chunk records a task
+// may hold.
+struct CascadeWgLayout {
+  int32_t off_len, off_gs, off_pl, off_gof, off_tpre, off_misc, off_mpre, off_rec, off_acc, off_ml;
+  int32_t words, capacity;
 };
 bool cascade_shape_supported(int head_dim, int block_size, int group, int num_seqs);
+// want_chunks (> 0) caps the records at what a task can need (0: as many as
+// the LDS holds).
+CascadeWgLayout cascade_wg_layout(int head_dim, int block_size, int num_seqs, int num_groups,
+                                  int64_t want_chunks);
 hipError_t launch_cascade(const CascadeLaunch& a, hipStream_t stream);
 
 // Paged prefill (causal multi-query attention).  The new tokens of sequence

@@ -293,6 +293,25 @@ def test_cascade_workspace_size_rules():
     assert cws(_dims(num_seqs=0), 0, 0) >= 0
 
 
+def test_cascade_plan_kernel_rules():
+    """AUTO runs the one-launch workgroup form when a task's chunks (the
+    longest prefix plus its members' longest suffixes) fit its LDS records,
+    else the two-launch form; STREAM_WG asks for the first, MFMA for the
+    second."""
+    plan = lambda d, ng=1, lp=32, bs=16: pkv.lib().pkv_cascade_plan_kernel(ctypes.byref(d), ng, lp,
+                                                                         bs)
+    assert plan(_dims()) == 4
+    assert plan(_dims(kernel=4)) == 4
+    assert plan(_dims(kernel=1)) == 1
+    assert plan(_dims(head_dim=128)) == 4
+    # 4 sequences of up to 1 M tokens: a task's suffix chunks outgrow LDS
+    big = dict(num_seqs=4, max_seq_len=1 << 20, max_blocks_per_seq=1 << 16, num_blocks=1 << 18)
+    assert plan(_dims(**big)) == 1
+    assert plan(_dims(kernel=4, **big)) == -1
+    assert plan(_dims(kernel=7)) == -1  # not a kernel family
+    assert plan(_dims(head_dim=80)) == -1
+
+
 def test_cascade_rejects_before_any_hip_call():
     lib = pkv.lib()
     dims = _dims()

@@ -37,8 +37,11 @@ def _product(w):
     return kc, vc
 
 
+KERNELS = ["stream_wg", "mfma"]  # one launch (workgroup per task), two launches (items + merge)
+
+
 def _cascade(w, kc, vc, out_dtype, seq_lens=None, group_starts=None, prefix_lens=None,
-             max_prefix_len=None):
+             max_prefix_len=None, kernel="auto"):
     lens = w.seq_lens if seq_lens is None else seq_lens
     gs = w.extra["group_starts"] if group_starts is None else group_starts
     pl = w.extra["prefix_lens"] if prefix_lens is None else prefix_lens
@@ -49,7 +52,7 @@ def _cascade(w, kc, vc, out_dtype, seq_lens=None, group_starts=None, prefix_lens
         torch.from_numpy(np.asarray(gs, np.int32)).to(DEV),
         torch.from_numpy(np.asarray(pl, np.int32)).to(DEV), w.block_size, w.scale, out,
         max_prefix_len=int(max(pl)) if max_prefix_len is None else max_prefix_len,
-        max_seq_len=int(max(w.seq_lens.max(), 1)))
+        max_seq_len=int(max(w.seq_lens.max(), 1)), kernel=kernel)
     torch.cuda.synchronize()
     return out
 
@@ -75,28 +78,30 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("name", list(CASES))
-def test_cascade_small(name):
+def test_cascade_small(name, kernel):
     seed, sizes, pblocks, hq, hkv, d, bs, mx, mn, empty = CASES[name]
-    say(f"case cascade {name}")
+    say(f"case cascade {name} {kernel}")
     w = workloads.shared_prefix_small(seed, sizes, pblocks, hq, hkv, d, bs, mx, mn, empty)
     ref = _reference(w)
     kc, vc = _product(w)
-    out32 = _cascade(w, kc, vc, torch.float32).cpu().numpy()
-    compare(out32, ref, strict_abs=True, what=f"{name}/f32")
-    out16 = _cascade(w, kc, vc, torch.bfloat16).float().cpu().numpy()
-    compare(out16, ref, strict_abs=False, what=f"{name}/bf16")
+    out32 = _cascade(w, kc, vc, torch.float32, kernel=kernel).cpu().numpy()
+    compare(out32, ref, strict_abs=True, what=f"{name}/{kernel}/f32")
+    out16 = _cascade(w, kc, vc, torch.bfloat16, kernel=kernel).float().cpu().numpy()
+    compare(out16, ref, strict_abs=False, what=f"{name}/{kernel}/bf16")
     if empty:
         assert np.all(out32[-1] == 0)
     # the same bits on a second call
-    again = _cascade(w, kc, vc, torch.float32).cpu().numpy()
+    again = _cascade(w, kc, vc, torch.float32, kernel=kernel).cpu().numpy()
     np.testing.assert_array_equal(out32, again)
 
 
-def test_cascade_no_sharing_equals_plain_decode_rule():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_cascade_no_sharing_equals_plain_decode_rule(kernel):
     """Every sequence its own group with no prefix: all work is suffix items,
     which must still agree with the oracle (and T = 1 gives v_0 exactly)."""
-    say("case cascade singletons")
+    say(f"case cascade singletons {kernel}")
     w = workloads.shared_prefix_small(7, [1] * 9, [0] * 9, 8, 2, 64, 16, 130, 1, False)
     # shorten sequence 0 to its first token (its other rows leave the logical list)
     keep = np.ones(len(w.k_tok), bool)
@@ -106,38 +111,39 @@ def test_cascade_no_sharing_equals_plain_decode_rule():
     w.extra["repeat_rows"] = w.extra["repeat_rows"][keep]
     ref = _reference(w)
     kc, vc = _product(w)
-    out = _cascade(w, kc, vc, torch.float32).cpu().numpy()
-    compare(out, ref, strict_abs=True, what="singletons/f32")
+    out = _cascade(w, kc, vc, torch.float32, kernel=kernel).cpu().numpy()
+    compare(out, ref, strict_abs=True, what=f"singletons/{kernel}/f32")
     v0 = oracle.widen_bf16(w.v_tok[0])
     np.testing.assert_array_equal(out[0], np.repeat(v0, 4, axis=0))
 
 
-def test_cascade_device_preconditions_give_nan():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_cascade_device_preconditions_give_nan(kernel):
     """Conditions only the device can see, turned into all-NaN outputs by the
     kernel's own checks: a member shorter than its group's prefix, a prefix
     that is not whole blocks, groups that do not end at S."""
-    say("case cascade device-side violations")
+    say(f"case cascade device-side violations {kernel}")
     w = workloads.shared_prefix_small(1, [3, 1, 5, 2], [4, 0, 6, 2], 16, 4, 64, 16, 150, 0, True)
     kc, vc = _product(w)
     short = w.seq_lens.copy()
     short[4] = 3 * 16  # group 2's prefix is 96 tokens
-    out = _cascade(w, kc, vc, torch.float32, seq_lens=short).cpu().numpy()
+    out = _cascade(w, kc, vc, torch.float32, seq_lens=short, kernel=kernel).cpu().numpy()
     assert np.all(np.isnan(out))
     pl = w.extra["prefix_lens"].copy()
     pl[0] = 40  # not a multiple of 16
-    out = _cascade(w, kc, vc, torch.float32, prefix_lens=pl).cpu().numpy()
+    out = _cascade(w, kc, vc, torch.float32, prefix_lens=pl, kernel=kernel).cpu().numpy()
     assert np.all(np.isnan(out))
     gs = w.extra["group_starts"].copy()
     gs[-1] -= 1
-    out = _cascade(w, kc, vc, torch.float32, group_starts=gs).cpu().numpy()
+    out = _cascade(w, kc, vc, torch.float32, group_starts=gs, kernel=kernel).cpu().numpy()
     assert np.all(np.isnan(out))
     pl = w.extra["prefix_lens"].copy()
     out = _cascade(w, kc, vc, torch.float32, prefix_lens=pl,
-                   max_prefix_len=int(pl.max()) - 16).cpu().numpy()
+                   max_prefix_len=int(pl.max()) - 16, kernel=kernel).cpu().numpy()
     assert np.all(np.isnan(out))
     # and a valid call afterwards is unaffected
-    out = _cascade(w, kc, vc, torch.float32).cpu().numpy()
-    compare(out, _reference(w), strict_abs=True, what="after violations/f32")
+    out = _cascade(w, kc, vc, torch.float32, kernel=kernel).cpu().numpy()
+    compare(out, _reference(w), strict_abs=True, what=f"after violations/{kernel}/f32")
 
 
 def test_cascade_prefix_sharing_workload():
@@ -181,6 +187,11 @@ def test_cascade_prefix_sharing_workload():
     w.block_tables = bm.block_table_array(seqs, pad=0)
     w.extra = dict(group_starts=gs, prefix_lens=pl)
     ref = _reference(w)
-    for dt in (torch.float32, torch.bfloat16):
-        out = _cascade(w, kc, vc, dt).float().cpu().numpy()
-        compare(out, ref, strict_abs=dt == torch.float32, what=f"prefix_cow cascade/{dt}")
+    assert pkv.cascade_plan_kernel(bits_to_bf16(w.q).to(DEV), kc,
+                                   torch.from_numpy(w.block_tables).to(DEV), len(pl),
+                                   int(pl.max()), max_seq_len=int(w.seq_lens.max())) == "stream_wg"
+    for kernel in KERNELS:
+        for dt in (torch.float32, torch.bfloat16):
+            out = _cascade(w, kc, vc, dt, kernel=kernel).float().cpu().numpy()
+            compare(out, ref, strict_abs=dt == torch.float32,
+                    what=f"prefix_cow cascade/{kernel}/{dt}")
