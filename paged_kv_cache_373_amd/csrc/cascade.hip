@@ -487,10 +487,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   int* s_len = lds + lay.off_len;    // [S] seq_lens
   int* s_gs = lds + lay.off_gs;      // [NG + 1] group_starts
   int* s_pl = lds + lay.off_pl;      // [NG] prefix_lens
-  int* s_gof = lds + lay.off_gof;    // [S] group of sequence b
   int* s_tpre = lds + lay.off_tpre;  // [NG + 1] tasks before group g's
   int* s_misc = lds + lay.off_misc;  // [NW] scan partials, [NW] error flag
-  int* s_mpre = lds + lay.off_mpre;  // [kCascadeRows + 1] suffix chunks before member m's
   int* s_rec = lds + lay.off_rec;    // [capacity][kRec] the task's chunk records
   float* s_acc = reinterpret_cast<float*>(lds + lay.off_acc);  // [NW][16][D]
   float* s_ml = reinterpret_cast<float*>(lds + lay.off_ml);    // [NW][16][max, sum]
@@ -506,36 +504,118 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   // prefixes are whole blocks within the host's bound, no member is shorter
   // than its group's prefix or longer than the host's bound).  Every
   // workgroup reaches the same verdict; a violation makes every row NaN.
-  for (int i = tid; i < S; i += NTH) s_len[i] = a.seq_lens[i];
-  for (int i = tid; i <= NG; i += NTH) s_gs[i] = a.group_starts[i];
-  for (int i = tid; i < NG; i += NTH) s_pl[i] = a.prefix_lens[i];
-  if (tid == 0) s_misc[NW] = 0;
-  __syncthreads();
-  for (int g = tid; g < NG; g += NTH) {
-    const int b0 = s_gs[g];
-    const int b1 = s_gs[g + 1];
-    const int L = s_pl[g];
-    const bool bad = b0 < 0 || b1 <= b0 || b1 > S || (g == 0 && b0 != 0) ||
-                     (g == NG - 1 && b1 != S) || L < 0 || L % BS != 0 ||
-                     L > a.max_prefix_len;
-    if (bad) {
-      s_misc[NW] = 1;
-    } else {
-      for (int b = b0; b < b1; ++b) s_gof[b] = g;
+  if (S <= NTH && NG < 64) {
+    // A batch of at most NTH sequences in at most 63 groups: every wavefront
+    // loads the groups' starts, ends and prefixes into its lanes (lane g:
+    // group g) and thread b the length of sequence b, all in one round trip;
+    // the checks are ballots and the task prefix a scalar loop, with one
+    // barrier.  Each wavefront flags a violation in a word of its own.
+    const int ls = a.seq_lens[min(tid, S - 1)];
+    const int gs0 = a.group_starts[min(lane, NG)];
+    const int gs1 = a.group_starts[min(lane + 1, NG)];
+    const int pl = a.prefix_lens[min(lane, NG - 1)];
+    // group `lane`: a run of members starting where the previous one ends,
+    // its prefix whole blocks within the host's bound
+    bool bad = false;
+    if (lane < NG)
+      bad = (gs0 < 0) | (gs1 <= gs0) | (gs1 > S) | ((lane == 0) & (gs0 != 0)) |
+            ((lane == NG - 1) & (gs1 != S)) | (pl < 0) | (pl % BS != 0) |
+            (pl > a.max_prefix_len);
+    // sequence tid: its group (the groups after the first whose start is
+    // <= tid), no shorter than that group's prefix, within the host's bound
+    int grp = 0;
+    for (int g = 1; g < NG; ++g) grp += __builtin_amdgcn_readlane(gs0, g) <= tid ? 1 : 0;
+    const int plb = __shfl(pl, grp);
+    if (tid < S) {
+      s_len[tid] = ls;
+      bad = bad | (ls < plb) | (ls > a.max_seq_len);
     }
-  }
-  __syncthreads();
-  if (s_misc[NW] == 0) {
+    const int F = gs1 - gs0;
+    const int cnt = (lane < NG && F > 0 && F <= S) ? Hkv * div_up(F, mpt) : 0;
+    if (w == 0) {
+      if (lane <= NG) s_gs[lane] = gs0;
+      if (lane < NG) s_pl[lane] = pl;
+      // tasks before group g (lane g), Hkv ceil(F_g / mpt) per group
+      int run = 0, mine = 0;
+      for (int g = 0; g < NG; ++g) {
+        mine = lane == g ? run : mine;
+        run += __builtin_amdgcn_readlane(cnt, g);
+      }
+      if (lane < NG) s_tpre[lane] = mine;
+      if (lane == 0) s_tpre[NG] = run;
+    }
+    const bool any_bad = __ballot(bad) != 0;  // (every lane takes part)
+    if (lane == 0) s_misc[NW + w] = any_bad ? 1 : 0;
+    __syncthreads();
+  } else {
+    // The three arrays' first NTH entries are loaded together (clamped
+    // indices, no branch around the loads), so the set-up waits for one round
+    // trip rather than three.
+    {
+      const int ls = a.seq_lens[min(tid, S - 1)];
+      const int lg = a.group_starts[min(tid, NG)];
+      const int lp = a.prefix_lens[min(tid, NG - 1)];
+      if (tid < S) s_len[tid] = ls;
+      if (tid <= NG) s_gs[tid] = lg;
+      if (tid < NG) s_pl[tid] = lp;
+      for (int i = tid + NTH; i < S; i += NTH) s_len[i] = a.seq_lens[i];
+      for (int i = tid + NTH; i <= NG; i += NTH) s_gs[i] = a.group_starts[i];
+      for (int i = tid + NTH; i < NG; i += NTH) s_pl[i] = a.prefix_lens[i];
+    }
+    if (tid < NW) s_misc[NW + tid] = 0;
+    __syncthreads();
+    // Group g (thread g): a run of members starting where the previous one
+    // ends, its prefix whole blocks within the host's bound.
+    for (int g = tid; g < NG; g += NTH) {
+      const int b0 = s_gs[g];
+      const int b1 = s_gs[g + 1];
+      const int L = s_pl[g];
+      const bool bad = b0 < 0 || b1 <= b0 || b1 > S || (g == 0 && b0 != 0) ||
+                       (g == NG - 1 && b1 != S) || L < 0 || L % BS != 0 ||
+                       L > a.max_prefix_len;
+      if (bad) s_misc[NW] = 1;
+    }
+    // Sequence b (thread b): its group (the last whose start is <= b; some
+    // group in [0, NG) even when the starts are not a partition, which the
+    // group checks flag), no shorter than that group's prefix, within the
+    // host's bound.
     for (int b = tid; b < S; b += NTH) {
+      int lo = 0, hi = NG;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_gs[mid] <= b) lo = mid; else hi = mid;
+      }
       const int T = s_len[b];
-      if (T < s_pl[s_gof[b]] || T > a.max_seq_len) s_misc[NW] = 1;
+      if (T < s_pl[lo] || T > a.max_seq_len) s_misc[NW] = 1;
     }
-    block_scan<NTH>(
-        NG, [&](int g) { return Hkv * div_up(s_gs[g + 1] - s_gs[g], mpt); }, s_tpre, s_misc,
-        tid);
+    // Tasks before each group, Hkv ceil(F_g / mpt) per group (a group of no
+    // members or more than S counts none; the checks above flag it).
+    auto group_tasks = [&](int g) __attribute__((always_inline)) {
+      const int F = s_gs[g + 1] - s_gs[g];
+      return F > 0 && F <= S ? Hkv * div_up(F, mpt) : 0;
+    };
+    if (NG <= 64) {
+      // one wavefront's scan, lane g holding group g
+      if (tid < 64) {
+        const int mine = tid < NG ? group_tasks(tid) : 0;
+        int incl = mine;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off);
+          if (tid >= off) incl += y;
+        }
+        if (tid < NG) s_tpre[tid + 1] = incl;
+        if (tid == 0) s_tpre[0] = 0;
+      }
+      __syncthreads();
+    } else {
+      block_scan<NTH>(NG, group_tasks, s_tpre, s_misc, tid);
+    }
   }
-  __syncthreads();
-  if (s_misc[NW] != 0) {
+  int flagged = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) flagged |= s_misc[NW + i];
+  if (flagged != 0) {
     for (int b = blockIdx.x; b < S; b += gridDim.x)
       for (int e = tid; e < Hq * D; e += NTH)
         store_out(a.out, static_cast<size_t>(b) * Hq * D + e, NAN, a.out_f32);
@@ -572,16 +652,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     const int m0 = (rem - h * nblk) * mpt;
     const int mc = min(mpt, F - m0);  // members of this task
     const int nP = div_up(L, 32);     // prefix chunks
-    if (tid == 0) {
-      int run = 0;
-      for (int m = 0; m < mc; ++m) {
-        s_mpre[m] = run;
-        run += div_up(s_len[b0 + m0 + m] - L, 32);
-      }
-      s_mpre[mc] = run;
-    }
-    __syncthreads();
-    const int n = nP + s_mpre[mc];  // the task's chunks
+    // Suffix chunks of the task's members (every thread reads the mc <= 16
+    // lengths itself, so no barrier is needed here).
+    int nsuf = 0;
+    for (int m = 0; m < mc; ++m) nsuf += div_up(s_len[b0 + m0 + m] - L, 32);
+    const int n = nP + nsuf;  // the task's chunks
     if (n > lay.capacity) {
       // (cannot happen for lengths within the host's bounds, which size the
       // launch; a task past them gets NaN rows rather than records past LDS)
@@ -606,12 +681,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
         last_blk = (L - 1) / BS;
         s_rec[i * kRec + 1] = min(32, L - tok0);
       } else {
-        const int j = i - nP;
+        // suffix chunk j: member m's chunk j - (suffix chunks before m)
+        int j = i - nP;
         int m = 0;
-        while (m + 1 < mc && s_mpre[m + 1] <= j) ++m;
-        const int T = s_len[b0 + m0 + m];
+        int T = s_len[b0 + m0];
+        for (int cnt = div_up(T - L, 32); j >= cnt && m + 1 < mc; cnt = div_up(T - L, 32)) {
+          j -= cnt;
+          ++m;
+          T = s_len[b0 + m0 + m];
+        }
         member = m;
-        tok0 = L + 32 * (j - s_mpre[m]);
+        tok0 = L + 32 * j;
         row = a.block_tables + static_cast<size_t>(b0 + m0 + m) * MB;
         last_blk = (T - 1) / BS;
         s_rec[i * kRec + 1] = min(32, T - tok0);
@@ -829,14 +909,10 @@ CascadeWgLayout cascade_wg_layout(int head_dim, int block_size, int num_seqs, in
   w = up4(w + num_groups + 1);
   lay.off_pl = w;
   w = up4(w + num_groups);
-  lay.off_gof = w;
-  w = up4(w + num_seqs);
   lay.off_tpre = w;
   w = up4(w + num_groups + 1);
   lay.off_misc = w;
   w = up4(w + 2 * nw);
-  lay.off_mpre = w;
-  w = up4(w + kCascadeRows + 1);
   lay.off_acc = w;
   w = up4(w + static_cast<int64_t>(nw) * kCascadeRows * head_dim);
   lay.off_ml = w;

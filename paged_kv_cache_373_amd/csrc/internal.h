@@ -168,7 +168,7 @@ struct CascadeLaunch {
 // LDS of the workgroup form, in 4-byte words; capacity = chunk records a task
 // may hold.
 struct CascadeWgLayout {
-  int32_t off_len, off_gs, off_pl, off_gof, off_tpre, off_misc, off_mpre, off_rec, off_acc, off_ml;
+  int32_t off_len, off_gs, off_pl, off_tpre, off_misc, off_rec, off_acc, off_ml;
   int32_t words, capacity;
 };
 bool cascade_shape_supported(int head_dim, int block_size, int group, int num_seqs);
