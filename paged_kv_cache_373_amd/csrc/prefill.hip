@@ -21,8 +21,8 @@
 // per-row causal limit.  It takes three neighbouring tiles at a time at
 // head_dim 64 (one at 128, whose operands take twice the registers): each
 // chunk loaded serves all of them, and their steps interleave.  The tiles of a (sequence, KV head)
-// run latest first, so the longest causal ranges start first; the four
-// wavefronts of a workgroup take neighbouring tiles, which read the same
+// run latest first, so the longest causal ranges start first; neighbouring
+// workgroups of one wavefront each take neighbouring tiles, which read the same
 // chunks.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -34,7 +34,11 @@
 namespace pkv {
 namespace {
 
-constexpr int kNW = 4;  // wavefronts per workgroup
+// Wavefronts per workgroup: one.  Measured on the chunked Llama step (same
+// process, alternating trials): one 77.0-79.3 us, two 80.4-81.5, four
+// 83.1-85.1, eight 94.2-95.2; with single-wavefront workgroups the
+// dispatcher fills each SIMD's free slot with whatever item comes next.
+constexpr int kNW = 1;
 
 // 16-row tiles a wavefront takes at a time: three at head_dim 64 (measured
 // against one, two and four on the chunked Llama step: 100 us against 180,
