@@ -75,6 +75,22 @@ __device__ __forceinline__ float maxnan(float a, float b, float c) {
   return maxnan(maxnan(a, b), c);
 }
 
+// Inclusive sum over lanes 0 .. lane of the wavefront, in registers: a
+// Hillis-Steele scan inside each 16-lane row (row shifts by 1, 2, 4, 8 with
+// zeros shifted in), then row 0's total added to row 1 and row 2's to row 3
+// (broadcast of lane 15 of the row before), then lane 31's running total to
+// rows 2 and 3.  Six data-parallel-primitive adds, no trip through the LDS
+// crossbar as a shuffle takes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+
 // Maximum over the four 16-lane rows of the wavefront at each lane's column
 // (lanes r, 16 + r, 32 + r and 48 + r), on every lane.  The two row-swap
 // instructions of gfx950 pair rows (0,1) and (2,3), then halves (0,1) and

@@ -113,7 +113,30 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
   // middle-unit counter starts at zero; the prefix's barriers order this
   // before the first window's records.)
   if (tid == 0) s_misc[3] = 0;
-  chunk_prefix<NTH>(seq_lens, S, s_len, s_pre, s_wsum, tid);
+  // A batch of at most 64 sequences keeps them in the lanes of every
+  // wavefront (lane b: T_b and the chunks before sequence b), scanned in
+  // registers, with one barrier after wavefront 0 has stored them; larger
+  // batches take the general prefix.  The lanes also serve the records'
+  // search below.
+  const bool lanes_hold = S <= 64;
+  int lane_len = 0, lane_pre = 0;
+  if (lanes_hold) {
+    const int T = seq_lens[min(lane, S - 1)];
+    lane_len = lane < S ? T : 0;
+    const int nbl = (lane_len + 31) >> 5;
+    const int incl = wave_incl_scan(nbl);
+    lane_pre = incl - nbl;
+    if (tid < 64) {
+      if (lane < S) {
+        s_len[lane] = lane_len;
+        s_pre[lane] = lane_pre;
+      }
+      if (lane == S - 1) s_pre[S] = incl;
+    }
+    __syncthreads();
+  } else {
+    chunk_prefix<NTH>(seq_lens, S, s_len, s_pre, s_wsum, tid);
+  }
   const int64_t C = static_cast<int64_t>(Hkv) * s_pre[S];
   const int64_t NWG = gridDim.x;
   const int64_t per_group = (C + NWG - 1) / NWG;
@@ -194,9 +217,37 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     // from its own position and index alone.  The entries of the units
     // between go to a list as well, in any order.
     {
+      // With the sequences in the lanes, a chunk's sequence is the last one
+      // of the window's span whose prefix (times Hkv) is <= the chunk: the
+      // span's ends from two ballots, then a short walk over it per lane.
+      int span0 = 0, span1 = 0;
+      if (lanes_hold) {
+        const int64_t hp = static_cast<int64_t>(Hkv) * lane_pre;
+        span0 = __popcll(__ballot(lane < S && hp <= ws)) - 1;
+        span1 = __popcll(__ballot(lane < S && hp <= ws + n - 1)) - 1;
+      }
       for (int t = tid; t < n; t += NTH) {
         int b, h, lc;
-        locate(ws + t, b, h, lc);
+        if (lanes_hold) {
+          const int64_t cc = ws + t;
+          b = span0;
+          int pb = __builtin_amdgcn_readlane(lane_pre, span0);
+          int tb = __builtin_amdgcn_readlane(lane_len, span0);
+          for (int j = span0 + 1; j <= span1; ++j) {
+            const int pj = __builtin_amdgcn_readlane(lane_pre, j);
+            if (static_cast<int64_t>(Hkv) * pj <= cc) {
+              b = j;
+              pb = pj;
+              tb = __builtin_amdgcn_readlane(lane_len, j);
+            }
+          }
+          const int nb = (tb + 31) >> 5;
+          const int rem = static_cast<int>(cc - static_cast<int64_t>(Hkv) * pb);
+          h = rem / nb;
+          lc = rem - h * nb;
+        } else {
+          locate(ws + t, b, h, lc);
+        }
         const int T = s_len[b];
         const int nb = (T + 31) >> 5;
         const int valid = min(32, T - 32 * lc);
