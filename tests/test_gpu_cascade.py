@@ -146,6 +146,48 @@ def test_cascade_device_preconditions_give_nan(kernel):
     compare(out, _reference(w), strict_abs=True, what=f"after violations/{kernel}/f32")
 
 
+# Shapes past the one-launch form's lane-held set-up (at most 256 sequences in at
+# most 63 groups): its general path keeps the lengths and groups in LDS and scans them
+# with the whole workgroup.
+GENERAL = {
+    # 70 groups of one or two members, prefixes of 0..3 blocks
+    "groups70": (11, [1 + (g % 2) for g in range(70)], [g % 4 for g in range(70)], 8, 2, 64, 16,
+                 60, 0, False),
+    # 300 sequences in 3 groups
+    "seqs300": (12, [120, 100, 80], [3, 1, 2], 8, 2, 64, 16, 40, 0, True),
+}
+
+
+@pytest.mark.parametrize("name", list(GENERAL))
+def test_cascade_general_setup(name):
+    seed, sizes, pblocks, hq, hkv, d, bs, mx, mn, empty = GENERAL[name]
+    say(f"case cascade general set-up {name}")
+    w = workloads.shared_prefix_small(seed, sizes, pblocks, hq, hkv, d, bs, mx, mn, empty)
+    assert len(w.extra["prefix_lens"]) >= 64 or w.num_seqs > 256
+    ref = _reference(w)
+    kc, vc = _product(w)
+    assert pkv.cascade_plan_kernel(bits_to_bf16(w.q).to(DEV), kc,
+                                   torch.from_numpy(w.block_tables).to(DEV),
+                                   len(w.extra["prefix_lens"]), int(max(w.extra["prefix_lens"])),
+                                   max_seq_len=int(w.seq_lens.max())) == "stream_wg"
+    out = _cascade(w, kc, vc, torch.float32, kernel="stream_wg").cpu().numpy()
+    compare(out, ref, strict_abs=True, what=f"{name}/stream_wg/f32")
+    if empty:
+        assert np.all(out[-1] == 0)
+    # a member shorter than its group's prefix: every row NaN, then a valid call again
+    short = w.seq_lens.copy()
+    b = int(np.argmax(np.asarray(w.extra["prefix_lens"])[np.searchsorted(
+        w.extra["group_starts"], np.arange(w.num_seqs), side="right") - 1]))
+    pl_b = int(np.asarray(w.extra["prefix_lens"])[np.searchsorted(
+        w.extra["group_starts"], b, side="right") - 1])
+    assert pl_b > 0
+    short[b] = pl_b - 1
+    bad = _cascade(w, kc, vc, torch.float32, seq_lens=short, kernel="stream_wg").cpu().numpy()
+    assert np.all(np.isnan(bad))
+    again = _cascade(w, kc, vc, torch.float32, kernel="stream_wg").cpu().numpy()
+    np.testing.assert_array_equal(out, again)
+
+
 def test_cascade_prefix_sharing_workload():
     """The copy-on-write workload end to end: 4 prompts x 1000 tokens, 16 forks
     each with 1..300 private tokens, built by the product's BlockManager; its

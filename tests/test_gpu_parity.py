@@ -159,10 +159,12 @@ def test_stream_wg_lengths_over_bound_give_nan():
     assert torch.isnan(out).all()
 
 
-@pytest.mark.parametrize("num_seqs", [2048, 2100])
+@pytest.mark.parametrize("num_seqs", [64, 65, 300, 2048, 2100])
 def test_many_short_sequences(num_seqs):
     """The stream kernel keeps every length in LDS up to 2048 sequences;
-    beyond that AUTO runs the partitioned kernel."""
+    beyond that AUTO runs the partitioned kernel.  64 sequences are the most
+    the workgroup kernel holds in its wavefronts' lanes; 65 and 300 take its
+    general set-up."""
     say(f"case many sequences S={num_seqs}")
     w = workloads.random_small(36, num_seqs, 8, 2, 64, 16, 40, min_len=0)
     g, o = GpuSide(w), OracleSide(w)
