@@ -77,7 +77,8 @@ typedef enum { PKV_DTYPE_BF16 = 0, PKV_DTYPE_F32 = 1 } pkv_dtype;
  *            head_dim 64 or 128, block_size 8/16/32, group <= 16,
  *            num_seqs <= 2048.  Ignores partition_size.
  *   STREAM_WG  the same work dealt out in equal windows to whole workgroups
- *            (one per compute unit, 6 wavefronts at head_dim 64, 4 at 128)
+ *            (one per compute unit; at head_dim 64, 5 wavefronts when the call
+ *            declares no_shared_blocks, else 6; 4 at 128)
  *            whose wavefronts take the window's chunks one at a time, so they
  *            finish together; same shape limits.  A window holds as many
  *            chunks as the workgroup's LDS has slots for; when the chunk bound

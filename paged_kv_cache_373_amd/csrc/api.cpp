@@ -102,7 +102,7 @@ Plan plan_decode(const pkv_decode_dims* d, int32_t block_size) {
   // The workgroup stream kernel's launch: workgroups, and the windows each
   // walks when the chunk bound exceeds what its LDS holds at once.
   if (stream_ok) {
-    const int nw = pkv::wg_waves_per_group(d->head_dim);
+    const int nw = pkv::wg_waves_per_group(d->head_dim, d->no_shared_blocks != 0);
     int64_t groups = d->stream_waves > 0 ? (d->stream_waves + nw - 1) / nw : 0;
     if (groups == 0) {
       groups = (chunk_bound + kMinChunksPerGroup - 1) / kMinChunksPerGroup;

@@ -734,36 +734,43 @@ hipError_t launch_wg(const DecodeLaunch& a, int groups, const WgLayout& lay, siz
   return hipGetLastError();
 }
 
-template <int D, int NW>
+template <int D, int NWS, int NWC>
 hipError_t launch_wg_bs(const DecodeLaunch& a, int groups, const WgLayout& lay, size_t lds,
                         hipStream_t stream) {
   const bool st = a.prm.stream_kv != 0;
   switch (a.prm.block_size) {
     case 8:
-      return st ? launch_wg<D, 8, NW, true>(a, groups, lay, lds, stream)
-                : launch_wg<D, 8, NW, false>(a, groups, lay, lds, stream);
+      return st ? launch_wg<D, 8, NWS, true>(a, groups, lay, lds, stream)
+                : launch_wg<D, 8, NWC, false>(a, groups, lay, lds, stream);
     case 16:
-      return st ? launch_wg<D, 16, NW, true>(a, groups, lay, lds, stream)
-                : launch_wg<D, 16, NW, false>(a, groups, lay, lds, stream);
+      return st ? launch_wg<D, 16, NWS, true>(a, groups, lay, lds, stream)
+                : launch_wg<D, 16, NWC, false>(a, groups, lay, lds, stream);
     default:
-      return st ? launch_wg<D, 32, NW, true>(a, groups, lay, lds, stream)
-                : launch_wg<D, 32, NW, false>(a, groups, lay, lds, stream);
+      return st ? launch_wg<D, 32, NWS, true>(a, groups, lay, lds, stream)
+                : launch_wg<D, 32, NWC, false>(a, groups, lay, lds, stream);
   }
 }
 
 }  // namespace
 
-// Wavefronts per workgroup: at head_dim 64, six (two SIMDs with two, two
-// with one): measured against four to eight on the Llama-shaped batch of 64
-// (31.9 us against 32.5 us for eight, 32.0-32.5 us for four, five and
-// seven).  More bytes in flight per compute unit than six wavefronts hold
-// only lengthen the queues at the end of a window.  At head_dim 128, four.
-int wg_waves_per_group(int head_dim) { return head_dim <= 64 ? 6 : 4; }
+// Wavefronts per workgroup.  At head_dim 64 with streaming K/V loads (no
+// block shared in the call), five (one SIMD with two, three with one):
+// measured against four to eight on the Llama-shaped batch of 64 with the
+// lane-held set-up (30.50-30.56 us against 30.61-30.67 for six, 30.82 for
+// seven, 31.22 for eight, 31.91 for four); more bytes in flight per compute
+// unit only lengthen the queues at the end of a window.  With cached loads
+// (blocks shared across the call, many hits in L2), six: on the copy-on-write
+// batch five ran 28.35 us against 26.96 for six.  At head_dim 128, four.
+int wg_waves_per_group(int head_dim, bool stream_kv) {
+  return head_dim <= 64 ? (stream_kv ? 5 : 6) : 4;
+}
+// The most either choice uses (the LDS layout has room for it).
+static int wg_max_waves(int head_dim) { return head_dim <= 64 ? 6 : 4; }
 
 WgLayout wg_layout(int head_dim, int block_size, int group, int num_seqs, int max_windows) {
   WgLayout lay = {};
   const int nb = block_size >= 32 ? 1 : 32 / block_size;
-  const int nw = wg_waves_per_group(head_dim);
+  const int nw = wg_max_waves(head_dim);
   auto up4 = [](int w) { return (w + 3) / 4 * 4; };
   int w = 0;
   lay.off_len = w;
@@ -800,8 +807,8 @@ hipError_t launch_decode_wg(const DecodeLaunch& a, int num_groups, int max_windo
                                  max_windows);
   if (lay.capacity < 1) return hipErrorInvalidValue;
   const size_t lds = static_cast<size_t>(lay.words) * 4;
-  return a.prm.head_dim == 64 ? launch_wg_bs<64, 6>(a, num_groups, lay, lds, stream)
-                              : launch_wg_bs<128, 4>(a, num_groups, lay, lds, stream);
+  return a.prm.head_dim == 64 ? launch_wg_bs<64, 5, 6>(a, num_groups, lay, lds, stream)
+                              : launch_wg_bs<128, 4, 4>(a, num_groups, lay, lds, stream);
 }
 
 }  // namespace pkv

@@ -76,7 +76,7 @@ hipError_t launch_decode_mfma(const DecodeLaunch& a, int waves, hipStream_t stre
 hipError_t launch_decode_generic(const DecodeLaunch& a, hipStream_t stream);
 
 // Workgroup stream kernel.  One workgroup per compute unit holds
-// wg_waves_per_group(head_dim) wavefronts; its LDS (dynamic shared memory) is
+// wg_waves_per_group(head_dim, stream_kv) wavefronts; its LDS (dynamic shared memory) is
 // carved as below, in 4-byte words, with room for `capacity` chunks a window.
 constexpr int kWgLdsBytes = 160 * 1024;  // LDS a workgroup may use on gfx950
 constexpr int kWgMaxCapacity = 1024;     // chunks a window holds at most
@@ -86,7 +86,7 @@ struct WgLayout {
   int32_t off_len, off_pre, off_wsum, off_misc, off_rec, off_unit, off_list, off_acc, off_ml;
   int32_t words;        // total LDS words
 };
-int wg_waves_per_group(int head_dim);
+int wg_waves_per_group(int head_dim, bool stream_kv);
 WgLayout wg_layout(int head_dim, int block_size, int group, int num_seqs, int max_windows);
 hipError_t launch_decode_wg(const DecodeLaunch& a, int num_groups, int max_windows,
                             hipStream_t stream);
