@@ -670,6 +670,21 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
       continue;
     }
 
+    // The tile's query rows as the QK^T B operand: lane (c, r) holds dims
+    // [32 hs + 8 c, +8) of row r (member r / G, head r % G).  Rows past the
+    // task's members read member 0's row; they attend nothing (always masked)
+    // and are not written.  They load now, ahead of the records' table loads,
+    // so the first fold does not wait for them (0.1 us on prefix_cow).
+    const int rm = r / G;
+    const bool live = r < mc * G;
+    bf16x8_t qop[HS];
+    {
+      const uint16_t* qrow =
+          a.q + (static_cast<size_t>(b0 + m0 + (live ? rm : 0)) * Hq + h * G + (live ? r - rm * G : 0)) *
+                    D + 8 * c;
+#pragma unroll
+      for (int hs = 0; hs < HS; ++hs) qop[hs] = load_bf16x8(qrow + 32 * hs);
+    }
     // 3. The chunk records: member (-1: prefix), valid tokens, physical blocks.
     for (int i = tid; i < n; i += NTH) {
       int member, tok0, last_blk;
@@ -703,16 +718,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     }
     __syncthreads();
 
-    // 4. The tile's query rows as the QK^T B operand: lane (c, r) holds dims
-    // [32 hs + 8 c, +8) of row r (member r / G, head r % G).  Rows past the
-    // task's members read member 0's row; they attend nothing (always masked)
-    // and are not written.
-    const int rm = r / G;
-    const bool live = r < mc * G;
-    const uint16_t* qrow =
-        a.q + (static_cast<size_t>(b0 + m0 + (live ? rm : 0)) * Hq + h * G + (live ? r - rm * G : 0)) *
-                  D + 8 * c;
-    bf16x8_t qop[HS];
+    // 4. Loading and folding the task's chunks.
     const size_t head_off = static_cast<size_t>(h) * M::kTile;
     auto issue = [&](int pos, Slot& sl8) __attribute__((always_inline)) {
       const int* rec = s_rec + pos * kRec;
@@ -785,12 +791,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D 
     // again, so every refill issues its loads and the wait counts stay exact).
     const int nmine = n > w ? (n - w + NW - 1) / NW : 0;
     if (nmine > 0) {
-      // (the query rows load between the ring's two first chunks: the first
-      // fold then waits for the first chunk and the rows, not the second)
       Slot ring[2];
       issue(w, ring[0]);
-#pragma unroll
-      for (int hs = 0; hs < HS; ++hs) qop[hs] = load_bf16x8(qrow + 32 * hs);
       issue(nmine > 1 ? w + NW : w, ring[1]);
       for (int k = 0;;) {
         if (k >= nmine) break;
