@@ -76,6 +76,11 @@ __device__ __forceinline__ void step_tiles(const bf16x8_t (&qop)[TPW][D / 32],
       s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x.k[1][hs], qop[t][hs], s1[t], 0, 0, 0);
     }
   }
+  // The masks, maxima and exponentials run at raised wave priority: the
+  // other wavefront on the SIMD, which is most likely in its matrix-core
+  // products, yields issue slots to this one's vector work, and the two
+  // phases overlap more often (about 4 % on the chunked Llama step).
+  __builtin_amdgcn_s_setprio(1);
   const bool tail = valid < 32;  // wave-uniform
   const int lv = valid - 8 * c;  // tokens of this lane group still in range
   float xs[TPW][8];
@@ -130,6 +135,7 @@ __device__ __forceinline__ void step_tiles(const bf16x8_t (&qop)[TPW][D / 32],
 #pragma unroll
       for (int e = 0; e < 8; ++e) x.v[nt][e] = (e < lv) ? x.v[nt][e] : static_cast<__bf16>(0.f);
   }
+  __builtin_amdgcn_s_setprio(0);
   const bf16x8_t ones = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
