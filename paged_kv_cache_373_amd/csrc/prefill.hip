@@ -48,12 +48,15 @@ constexpr int prefill_tiles_per_wave(int head_dim) { return head_dim <= 64 ? 3 :
 
 // One chunk folded into the states of TPW tiles at once: the arithmetic of
 // Mfma<D, BS>::step for each tile, regrouped by phase - every tile's QK^T
-// products, then every tile's masks and row maxima, one uniform test for a
-// rescale in any tile (rare: the maximum moves past the margin), then every
+// products, then every tile's masks and per-lane maxima, one uniform test for
+// a rescale in any tile (rare: the maximum moves past the margin; only then
+// are the row maxima formed across lanes), then every
 // tile's exponentials and P.V products.  Each phase is one straight run of
 // independent instructions over the tiles, which the compiler interleaves;
 // per tile the operations and their order are the step's, so the results are
-// the same bits.  With kCausal, lim[t] is how many of the chunk's tokens the
+// the same bits (the rescale test, made on each lane's maximum rather than
+// its row's, picks the same chunks unless a row holds a NaN score, whose
+// output is NaN either way).  With kCausal, lim[t] is how many of the chunk's tokens the
 // lane's row of tile t may see.
 template <int D, int BS, int TPW, bool kCausal>
 __device__ __forceinline__ void step_tiles(const bf16x8_t (&qop)[TPW][D / 32],
@@ -103,14 +106,15 @@ __device__ __forceinline__ void step_tiles(const bf16x8_t (&qop)[TPW][D / 32],
     }
     cm[t] = maxnan(maxnan(xs[t][0], xs[t][1], xs[t][2]), maxnan(xs[t][3], xs[t][4], xs[t][5]),
                    maxnan(xs[t][6], xs[t][7]));
-    cm[t] = max_over_rows(cm[t]) * sl;
-    need = need || cm[t] > st[t].m2 + kRescaleThreshold;
+    // a lane tests its own eight scores against its row's running maximum;
+    // the maximum over the row's four lane groups is formed only for a rescale
+    need = need || cm[t] * sl > st[t].m2 + kRescaleThreshold;
   }
   if (__ballot(need) != 0) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      if (__ballot(cm[t] > st[t].m2 + kRescaleThreshold) != 0) {
-        const float mn = fmaxf(st[t].m2, cm[t]);
+      if (__ballot(cm[t] * sl > st[t].m2 + kRescaleThreshold) != 0) {
+        const float mn = fmaxf(st[t].m2, max_over_rows(cm[t]) * sl);
         const float alpha = fast_exp2(st[t].m2 - mn);  // 0 on the first chunk (m2 = -inf)
         st[t].m2 = mn;
 #pragma unroll
