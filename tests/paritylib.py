@@ -57,6 +57,22 @@ def compare(got: np.ndarray, ref: np.ndarray, *, strict_abs: bool, what: str) ->
     return stats
 
 
+def compare_bf16p(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str) -> None:
+    """The attention rule of compare(), except that an element beyond it passes
+    when it lies within `bound`: the error the kernels' bf16 softmax weights
+    allow for that element (derived where the bound is built).  Every element
+    beyond the rule is counted in the output."""
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    d = np.abs(got - ref)
+    beyond = (d > ABS_TOL) & (d > REL_TOL * np.abs(ref))
+    over = beyond & (d > bound)
+    say(f"  {what}: max_abs {d.max(initial=0.0):.3e}, beyond the {ABS_TOL:g}/{REL_TOL:g} rule "
+        f"{int(beyond.sum())} of {d.size} (all within the bf16-P bound: {not over.any()}), "
+        f"largest d/bound there {float((d[beyond] / bound[beyond]).max(initial=0.0)):.3f}")
+    assert not over.any(), what
+
+
 def token_positions(seq_lens: np.ndarray):
     seq = np.repeat(np.arange(len(seq_lens), dtype=np.int64), seq_lens)
     pos = np.concatenate([np.arange(t, dtype=np.int64) for t in seq_lens]) if len(seq_lens) \

@@ -11,7 +11,7 @@ import torch
 import oracle
 import paged_kv_cache_373_amd as pkv
 import workloads
-from paritylib import DEV, GpuSide, OracleSide, bits_to_bf16, compare, say
+from paritylib import DEV, GpuSide, OracleSide, bits_to_bf16, compare, compare_bf16p, say
 
 pytestmark = pytest.mark.gpu
 
@@ -144,19 +144,6 @@ def _bf16p_bound(w, ref):
     return 2.0 ** -8 * bound
 
 
-def _compare_bf16p(out, ref, bound, what):
-    """The spec rule, except that an element beyond it passes when it
-    lies within the bf16-P bound; every such element is counted."""
-    d = np.abs(np.asarray(out, np.float64) - ref)
-    assert np.all(np.isfinite(out)), what
-    beyond = (d > 5e-3) & (d > 1e-2 * np.abs(ref))
-    over = beyond & (d > bound)
-    say(f"  {what}: max_abs {d.max():.3e}, beyond the 5e-3/1e-2 rule {int(beyond.sum())} "
-        f"of {d.size} (all within the bf16-P bound: {not over.any()}), "
-        f"largest d/bound there {float((d[beyond] / bound[beyond]).max(initial=0.0)):.3f}")
-    assert not over.any(), what
-
-
 @pytest.mark.parametrize("scale", [0.125, 1.0, 10.0, 50.0])
 def test_prefill_softmax_scales(scale):
     import dataclasses
@@ -171,9 +158,9 @@ def test_prefill_softmax_scales(scale):
         compare(out16, ref, strict_abs=False, what=f"prefill scale {scale}/bf16")
     else:  # sharper softmax: the rule, or the bf16-P bound where it is wider
         bound = _bf16p_bound(w, ref)
-        _compare_bf16p(out, ref, bound, f"prefill scale {scale}/f32")
+        compare_bf16p(out, ref, bound, f"prefill scale {scale}/f32")
         # the bf16 output adds its own rounding, half an ulp of |out|
-        _compare_bf16p(out16, ref, bound + 2.0 ** -8 * np.abs(ref), f"prefill scale {scale}/bf16")
+        compare_bf16p(out16, ref, bound + 2.0 ** -8 * np.abs(ref), f"prefill scale {scale}/bf16")
     if scale == 50.0:
         # closed form: where a row's best visible score beats the second by a
         # wide margin the softmax is one-hot, and the output is that V row
