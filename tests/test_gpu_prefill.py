@@ -49,6 +49,8 @@ CASES = {
     "g16_d128_b16": (5, 3, 32, 2, 128, 16, 300, 50, 1, 0),
     "g1_d64_b32_one_token": (6, 6, 8, 8, 64, 32, 33, 1, 1, 0),       # the decode step
     "g2_d64_b16_ctx_batch": (7, 3, 4, 2, 64, 16, 1100, 20, 1, 1000),  # more than 64 blocks
+    "g4_d64_b16_s64": (8, 64, 8, 2, 64, 16, 90, 12, 1, 0),   # sequences ranked by length
+    "g4_d64_b16_s70": (9, 70, 8, 2, 64, 16, 90, 12, 1, 0),   # past 64: the batch's order
 }
 
 
