@@ -22,9 +22,11 @@
 // head_dim 64 (one at 128, whose operands take twice the registers): each
 // chunk loaded serves all of them, and their steps interleave.  The tiles of a (sequence, KV head)
 // run latest first and, in batches of up to 64, the sequences longest first,
-// so the longest causal ranges start first; neighbouring
-// workgroups of one wavefront each take neighbouring tiles, which read the same
-// chunks.
+// so the longest causal ranges start first; neighbouring workgroups take
+// neighbouring tiles, which read the same chunks.  A workgroup has two
+// wavefronts: the items nearly as long as the batch's longest are split
+// between them (two halves of the chunks, merged in LDS); the others are
+// folded by one wavefront while the other leaves.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -35,11 +37,20 @@
 namespace pkv {
 namespace {
 
-// Wavefronts per workgroup: one.  Measured on the chunked Llama step (same
-// process, alternating trials): one 77.0-79.3 us, two 80.4-81.5, four
-// 83.1-85.1, eight 94.2-95.2; with single-wavefront workgroups the
-// dispatcher fills each SIMD's free slot with whatever item comes next.
-constexpr int kNW = 1;
+// Wavefronts per workgroup: two, for one item.  An item whose chunk count is
+// within kSplitNum / kSplitDen of the batch's longest sequence's (and at
+// least kSplitMin) is split: the first wavefront folds its first half of
+// the chunks, the second the rest, and the two states are merged in LDS.
+// Every other item is folded by the first wavefront alone while the second
+// leaves at once, so its slot goes to the next workgroup.  The longest items
+// set the launch's time (on the chunked Llama step the longest wavefronts run
+// as long as the launch), and splitting them shortens that chain.
+constexpr int kNW = 2;
+constexpr int kSplitNum = 4, kSplitDen = 5, kSplitMin = 16;
+// The second wavefront's running maxima start at this finite value rather
+// than -inf: a row that sees none of its half's chunks keeps exp2(-inf) = 0
+// for its masked scores (with -inf a masked score would give NaN).
+constexpr float kEmptyMax = -1.0e30f;
 
 // 16-row tiles a wavefront takes at a time: three at head_dim 64 (measured
 // against one, two and four on the chunked Llama step: 100 us against 180,
@@ -185,6 +196,7 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
   // 74.5-75.2 us on the chunked Llama step, whose batch order puts a long
   // sequence late).  Larger batches keep their order.
   int b = br;
+  int t_top = 0;  // the longest sequence's length (0: not ranked, no item is split)
   if (a.num_seqs <= 64) {
     const int ln = threadIdx.x & 63;
     const int Tl = ln < a.num_seqs ? a.seq_lens[ln] : -1;
@@ -195,6 +207,8 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
     }
     const unsigned long long hit = __ballot(ln < a.num_seqs && rank == br);
     b = hit != 0 ? static_cast<int>(__builtin_ctzll(hit)) : br;
+    const unsigned long long top = __ballot(ln < a.num_seqs && rank == 0);
+    t_top = top != 0 ? __builtin_amdgcn_readlane(Tl, static_cast<int>(__builtin_ctzll(top))) : 0;
   }
   const int wblk = t8 - (t8 / W) * W;  // this workgroup's block of items within the pair
   const int lane = threadIdx.x & 63;
@@ -213,7 +227,11 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
   const int nq = q1 - q0;
   const int T = a.seq_lens[b];
   const int ntiles = (nq * G + 15) / 16;
-  const int wave0 = wblk * kNW + (threadIdx.x >> 6);
+  // This wavefront's index in the workgroup.  It is kept per lane: made
+  // uniform (readfirstlane), it let the compiler restructure the item loop
+  // and spill 25 registers from the chunk loop at two wavefronts per SIMD.
+  const int part = threadIdx.x >> 6;
+  const int wave0 = wblk * kNW + part;
   const int nwaves = W * kNW;
   if (nq > T || T > a.max_blocks_per_seq * BS) {
     for (int e = wave0 * 64 + lane; e < nq * G * D; e += nwaves * 64) {
@@ -233,11 +251,22 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
     Regs x;
   };
 
-  // A wavefront takes TPW neighbouring tiles at a time: each chunk it loads
-  // serves all of their rows, and their steps interleave.
+  // A workgroup takes TPW neighbouring tiles at a time (an item): each chunk
+  // a wavefront loads serves all of their rows, and their steps interleave.
+  // The second wavefront's states of a split item, for the merge:
+  // [TPW][4 NT accumulators + 4 sums + 1 maximum][64 lanes].
+  constexpr int kStWords = 4 * NT + 5;
+  __shared__ float s_part[TPW * kStWords * 64];
+  const int nk_top = (t_top + 31) / 32;
   const int nitems = (ntiles + TPW - 1) / TPW;
-  for (int j = wave0; j < nitems; j += nwaves) {
+  for (int j = wblk; j < nitems; j += W) {
     const int tile0 = (nitems - 1 - j) * TPW;  // latest tiles first
+    const int last_i = min(nq - 1, ((tile0 + TPW) * 16 - 1) / G);
+    const int pos_max = ctx + last_i;      // the item's last position
+    const int pos_min = ctx + (tile0 * 16) / G;  // and its first (every row sees up to here)
+    const int nk = pos_max / 32 + 1;       // chunks up to it
+    const bool split = nk >= kSplitMin && kSplitDen * nk >= kSplitNum * nk_top && nk_top > 0;
+    if (!split && part != 0) continue;
     // This lane's row (r) of tile t: new token i, head g; past nq the row is
     // a zero query whose output is dropped.
     int pos[TPW];
@@ -254,23 +283,25 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
 #pragma unroll
       for (int hs = 0; hs < HS; ++hs) qop[t][hs] = live ? load_bf16x8(qrow + 32 * hs) : bf16x8_t{};
     }
-    const int last_i = min(nq - 1, ((tile0 + TPW) * 16 - 1) / G);
-    const int pos_max = ctx + last_i;      // the item's last position
-    const int pos_min = ctx + (tile0 * 16) / G;  // and its first (every row sees up to here)
-    const int nk = pos_max / 32 + 1;       // chunks up to it
     const int last_blk = (min(T, 32 * nk) - 1) / BS;
     // a dead row (past nq) sees every chunk the item reads, so its state stays finite
 #pragma unroll
     for (int t = 0; t < TPW; ++t) pos[t] = pos[t] < 0 ? pos_max : pos[t];
     typename M::State st[TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) st[t].reset();
+    for (int t = 0; t < TPW; ++t) {
+      st[t].reset();
+      if (part != 0) st[t].m2 = kEmptyMax;
+    }
+    // This wavefront's chunks: all of them, or its half of a split item.
+    const int klo = (split && part != 0) ? nk / 2 : 0;
+    const int khi = (split && part == 0) ? nk / 2 : nk;
 
-    for (int k0 = 0; k0 < nk; k0 += kBatchChunks) {
+    for (int k0 = klo; k0 < khi; k0 += kBatchChunks) {
       // the batch's blocks, one per lane (clamped to the last one needed)
       const int first_blk = k0 * NB;
       const int bid = row_bt[min(first_blk + lane, last_blk)];
-      const int nkb = min(kBatchChunks, nk - k0);
+      const int nkb = min(kBatchChunks, khi - k0);
       auto issue = [&](int kb, Slot& sl8) {
         size_t base[NB];
 #pragma unroll
@@ -319,6 +350,49 @@ __global__ void __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(D
       }
     }
 
+    // A split item's two states: the second wavefront's through LDS into the
+    // first's.  Lane (c, r) holds row 4 c + i's accumulator (features
+    // 16 nt + r) and sum, and row r's maximum; both are taken to the larger
+    // maximum of the two (every row sees chunk 0, so one of them is real).
+    if (split) {
+      if (part != 0) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          float* sp = s_part + t * kStWords * 64 + lane;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sp[(4 * nt + i) * 64] = st[t].acc[nt][i];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sp[(4 * NT + i) * 64] = st[t].lsum[i];
+          sp[(4 * NT + 4) * 64] = st[t].m2;
+        }
+      }
+      __syncthreads();
+      if (part == 0) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          __builtin_amdgcn_sched_barrier(0);  // one tile's LDS reads at a time
+          const float* sp = s_part + t * kStWords * 64 + lane;
+          const float mb = sp[(4 * NT + 4) * 64];
+          const float mn = fmaxf(st[t].m2, mb);
+          const float fa = fast_exp2(st[t].m2 - mn);
+          const float fb = fast_exp2(mb - mn);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float fai = __shfl(fa, 4 * c + i);  // factors of row 4 c + i
+            const float fbi = __shfl(fb, 4 * c + i);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              st[t].acc[nt][i] = st[t].acc[nt][i] * fai + sp[(4 * nt + i) * 64] * fbi;
+            st[t].lsum[i] = st[t].lsum[i] * fai + sp[(4 * NT + i) * 64] * fbi;
+          }
+        }
+      }
+      __syncthreads();  // (the next item reuses the LDS)
+      if (part != 0) continue;
+    }
+
     // Lane (c, r) holds row 4 c + e of each tile: its accumulator for
     // features 16 nt + r and its sum, whose quotient is the output.
 #pragma unroll
@@ -359,14 +433,14 @@ bool prefill_shape_supported(int head_dim, int block_size, int group) {
 }
 
 hipError_t launch_prefill(const PrefillLaunch& a, int max_q_len, hipStream_t stream) {
-  // one wavefront per item (tiles of 16 rows, three per item at head_dim 64) of
-  // the longest sequence's rows (a longer one is still covered: the
-  // wavefronts stride over the items)
+  // one workgroup per item (tiles of 16 rows, three per item at head_dim 64)
+  // of the longest sequence's rows (a longer one is still covered: the
+  // workgroups stride over the items)
   const int tiles = (max_q_len * a.group + 15) / 16;
   const int tpw = prefill_tiles_per_wave(a.head_dim);
   const int items = (tiles + tpw - 1) / tpw;
   PrefillLaunch la = a;
-  la.wg_per_pair = (items + kNW - 1) / kNW;
+  la.wg_per_pair = items;  // one item per workgroup
   if (la.wg_per_pair < 1) la.wg_per_pair = 1;
   // eight workgroups (one per XCD) per group of eight (sequence, KV head)
   // pairs and item block; the ones past the last pair exit at once
