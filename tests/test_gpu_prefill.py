@@ -51,6 +51,9 @@ CASES = {
     "g2_d64_b16_ctx_batch": (7, 3, 4, 2, 64, 16, 1100, 20, 1, 1000),  # more than 64 blocks
     "g4_d64_b16_s64": (8, 64, 8, 2, 64, 16, 90, 12, 1, 0),   # sequences ranked by length
     "g4_d64_b16_s70": (9, 70, 8, 2, 64, 16, 90, 12, 1, 0),   # past 64: the batch's order
+    # long contexts: items of >= 16 chunks near the longest are split between two wavefronts
+    "g8_d128_b32_split": (10, 3, 16, 2, 128, 32, 700, 40, 20, 500),
+    "g4_d64_b8_split": (11, 4, 16, 4, 64, 8, 900, 60, 30, 600),
 }
 
 
