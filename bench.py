@@ -51,7 +51,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 ROTATE_BYTES = 1 << 30
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_373_amd", "csrc", f)
-                  for f in ("chunk.h", "decode.hip", "decode_wg.hip")]
+                  for f in ("chunk.h", "decode.hip", "decode_wg.hip", "api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 

@@ -37,11 +37,13 @@ int32_t default_partition(const pkv_decode_dims* d, int32_t block_size) {
 
 enum Family { kGeneric, kMfma, kStream, kStreamWg };
 
-// Wavefronts the stream kernel launches by default: every one resident from
-// the start on an MI355X (256 CUs) - 8 per CU at head_dim 64 (2 per SIMD), 4
-// per CU at head_dim 128, whose larger operands allow 1 per SIMD - which keeps
-// enough bytes in flight to saturate HBM; fewer when the problem is small.
-int32_t stream_wave_target(int32_t head_dim) { return head_dim <= 64 ? 2048 : 1024; }
+// Wavefronts the stream kernel launches by default: one per SIMD of an MI355X
+// (256 CUs x 4), every one resident from the start; fewer when the problem is
+// small.  At head_dim 64 two per SIMD were measured too: the longer streams of
+// one per SIMD publish half the pieces and keep enough bytes in flight (8
+// sequences of 16-32 K tokens: 82.3 -> 75.7 us; the 16-layer pool step at
+// B = 8 / 16 / 32 within -2 .. +3.5 % per layer).
+int32_t stream_wave_target(int32_t /*head_dim*/) { return 1024; }
 constexpr int32_t kMinChunksPerWave = 4;
 // The workgroup stream kernel launches one workgroup per compute unit of an
 // MI355X, fewer when a workgroup would get under this many chunks.
